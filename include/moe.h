@@ -1,0 +1,203 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed MoE layer forward.
+ *
+ * The layer (pages: "colibri" README, sections "The idea" and "What's
+ * implemented"; "iliria" README, section "What's implemented"):
+ *   1. a DeepSeek-V3-style sigmoid router (noaux_tc): sigmoid scores, a
+ *      correction bias used for selection only, group-limited top-k, weights
+ *      renormalised over the chosen experts and multiplied by
+ *      routed_scaling_factor -- or, for Granite-shaped layers ("Glacial" page),
+ *      a softmax top-k router;
+ *   2. batch-union grouping: every unique expert of the batch is read once and
+ *      applied to every position routed to it;
+ *   3. SwiGLU experts stored as packed int4 / packed int2 codes with per-row
+ *      scales (or bf16), dequantized on use;
+ *   4. the weighted combine of the routed experts plus the shared expert.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
+ *     memory; the library allocates nothing and keeps no global state, so it
+ *     is safe to call from several host threads on different streams.
+ *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
+ *     stream) and never synchronise: results are valid once the stream has
+ *     reached the enqueued work.  A device-side fault surfaces at the caller's
+ *     next synchronisation.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     rejected call launches nothing.  No C++ exception crosses this ABI.
+ *   - Row-major layouts throughout.  Packed codes run along the input axis
+ *     of an [out][in] matrix: int4 element i of a row sits in byte i/2, low
+ *     nibble first (bits 0-3 = even element), two's complement; int2 element i
+ *     sits in byte i/4 at bits 2(i%4)..2(i%4)+1, two's complement.  One fp32
+ *     scale per output row ("per-row scales", "colibri" README).
+ *   - Ties in every selection go to the lowest index; router outputs are in
+ *     rank order (descending score, then ascending expert index).
+ *   - Non-finite inputs are outside the contract.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null/misaligned pointer, inconsistent descriptor      */
+  MOE_EUNSUPPORTED = 2,  /* valid but outside what the kernels handle (shapes)    */
+  MOE_EWORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_bytes()           */
+  MOE_EHIP = 4           /* a HIP launch or runtime call failed                   */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I4 = 2, MOE_I2 = 3 } moe_dtype;
+
+typedef enum { MOE_ROUTER_SIGMOID_NOAUX_TC = 0, MOE_ROUTER_SOFTMAX_TOPK = 1 } moe_router;
+
+/* Layer shape and numerics (plain data, passed by host pointer). */
+typedef struct {
+  int32_t hidden;          /* H: model width                                          */
+  int32_t inter;           /* I: routed expert intermediate size                      */
+  int32_t n_experts;       /* E: routed experts (<= 1024)                             */
+  int32_t top_k;           /* k: experts per token (<= 32, <= E)                      */
+  int32_t router;          /* moe_router                                              */
+  int32_t n_group;         /* sigmoid router: contiguous expert groups (1 = none)     */
+  int32_t topk_group;      /* sigmoid router: groups kept per token                   */
+  float routed_scaling;    /* routed_scaling_factor (1.0 for softmax layers)          */
+  int32_t expert_dtype;    /* MOE_I4 | MOE_I2 | MOE_BF16                              */
+  int32_t act_dtype;       /* MOE_F32 | MOE_BF16: type of x; with MOE_BF16 the        */
+                           /* SwiGLU output h is rounded to bf16 before the down     */
+                           /* projection                                             */
+  int32_t n_shared;        /* 0 or 1 shared expert (intermediate size n_shared * I)   */
+  int32_t shared_dtype;    /* MOE_I4 | MOE_I2 | MOE_BF16                              */
+  float norm_eps;          /* RMSNorm epsilon used by moe_stack_forward               */
+} moe_layer_desc;
+
+/* One expert set: E routed experts, or the n_shared shared expert(s).
+ * Expert e's gate/up matrix is [2I rows][H] (rows 0..I-1 gate, I..2I-1 up) at
+ * gate_up + e*gate_up_stride bytes; its down matrix is [H rows][I] at
+ * down + e*down_stride.  Scales (fp32, one per row) likewise; NULL for bf16.
+ * Strides let the caller keep each expert as one contiguous blob (codes and
+ * scales side by side) or keep each tensor contiguous across experts.
+ * Code and scale rows must be 16-byte aligned. */
+typedef struct {
+  const void* gate_up;
+  int64_t gate_up_stride;
+  const float* gate_up_scale;
+  int64_t gate_up_scale_stride;
+  const void* down;
+  int64_t down_stride;
+  const float* down_scale;
+  int64_t down_scale_stride;
+} moe_expert_set;
+
+typedef struct {
+  const float* w_router;   /* [E][H] fp32                                   */
+  const float* bias;       /* [E] fp32 correction bias, nullable            */
+  moe_expert_set routed;   /* E experts of expert_dtype                     */
+  moe_expert_set shared;   /* n_shared experts of shared_dtype (if any)     */
+} moe_layer_weights;
+
+/* Bytes of workspace moe_layer_forward / moe_stack_forward / moe_route /
+ * moe_expert_ffn need for n_tokens tokens (or rows).  Host-only and pure.
+ * Returns 0 for an invalid descriptor. */
+size_t moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens);
+
+/* Router: logits z = x W_r^T accumulated in fp64, then selection.
+ * Sigmoid noaux_tc ("colibri" README, "What's implemented"): s = sigmoid(z);
+ * c = s + bias; groups are n_group contiguous ranges of E/n_group experts;
+ * a group scores the sum of its two largest c; the topk_group best groups are
+ * kept; the top_k largest c among their experts are chosen; topk_w[j] =
+ * s_j / sum(s over the chosen) * routed_scaling.
+ * Softmax top-k (Granite MoE layer, "Glacial" page): the top_k largest z are
+ * chosen; topk_w = softmax over the chosen z, times routed_scaling.
+ * x: [n_tokens][H] of act_dtype.  Outputs: topk_idx [n_tokens][k] int32,
+ * topk_w [n_tokens][k] fp32.  Errors: MOE_EINVAL (bad descriptor or pointer),
+ * MOE_EWORKSPACE. */
+moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float* bias,
+                     const void* x, int32_t n_tokens, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/* Batch-union grouping ("colibri" README, "What's implemented"): a stable
+ * counting sort of the flat slots f = t*top_k + j by expert.
+ *   counts[E]    slots per expert;  offsets[E+1] exclusive prefix sum;
+ *   entries[F]   the slots f, sorted by (expert, f);  inverse[F]: inverse[entries[p]] = p;
+ *   active[E]    experts with counts > 0, ascending (first n_active entries valid);
+ *   n_active[1]  their number.  F = n_tokens * top_k.
+ * Indices outside [0, E) are a caller error (MOE_EINVAL is not detectable on
+ * the host: such slots are dropped from every output).  ws/ws_bytes are
+ * unused (pass NULL/0). */
+moe_status moe_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t* topk_idx,
+                      int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
+                      int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes, void* stream);
+
+/* One expert (dequant-on-use SwiGLU; "iliria" README, "What's implemented")
+ * on a list of activation rows: y[i] = down(silu(gate x_t) * up x_t) with
+ * t = rows[i] / row_div (rows NULL: t = i).  shared = 0 selects routed expert
+ * `expert` of `set` (dtype expert_dtype, intermediate I); shared = 1 the shared
+ * expert (shared_dtype, intermediate n_shared*I; `expert` must be 0).
+ * x: [*][H] act_dtype; y: [n_rows][H] fp32.  Workspace: moe_workspace_bytes(d,
+ * n_rows). */
+moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, int32_t shared,
+                          int32_t expert, const void* x, const int32_t* rows, int32_t n_rows,
+                          int32_t row_div, float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole routed layer: route, bucket, apply each active expert once to all
+ * of its tokens, and combine: out[t] = sum_j topk_w[t][j] * FFN_{e_tj}(x_t)
+ * (j ascending) + shared(x_t).  x: [n_tokens][H] act_dtype; out: [n_tokens][H]
+ * fp32.  topk_idx_out / topk_w_out ([n_tokens][k]) are optional copies of the
+ * routing.  Workspace: moe_workspace_bytes(d, n_tokens). */
+moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+                             int32_t n_tokens, float* out, int32_t* topk_idx_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Stage timing hook for moe_layer_forward_ex: when non-NULL, `events` is a
+ * (host) array of 2*MOE_N_STAGES hipEvent_t handles; events[2s] is recorded on
+ * `stream` right before stage s and events[2s+1] right after it. */
+enum {
+  MOE_STAGE_ROUTE = 0,     /* router logits + selection                 */
+  MOE_STAGE_BUCKET = 1,    /* batch-union grouping                      */
+  MOE_STAGE_GATE_UP = 2,   /* expert gate/up + SwiGLU (routed + shared) */
+  MOE_STAGE_DOWN = 3,      /* expert down projections + combine         */
+  MOE_N_STAGES = 4
+};
+typedef struct {
+  void* const* events;     /* (host) [2*MOE_N_STAGES] hipEvent_t, nullable */
+} moe_launch_opts;
+
+moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_layer_weights* w,
+                                const void* x, int32_t n_tokens, float* out,
+                                int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                size_t ws_bytes, void* stream, const moe_launch_opts* opts);
+
+/* RMSNorm with unit gain, out = x / sqrt(mean(x^2) + eps), computed in fp64
+ * and rounded to fp32.  x, out: [n_tokens][hidden] fp32 (may alias). */
+moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* out,
+                       void* stream);
+
+/* A pre-norm residual stack of n_layers MoE layers of one shape:
+ * for each layer l: y_l = MoE_l(RMSNorm(x)); x = x + y_l.
+ * layers: (host) array of n_layers weight sets; x: [n_tokens][H] fp32, input
+ * of layer 0 on entry and the final residual stream on return (act_dtype
+ * must be MOE_F32).  y_layers: optional [n_layers][n_tokens][H] fp32 copy of
+ * every layer's MoE output.  Workspace: moe_workspace_bytes(d, n_tokens). */
+moe_status moe_stack_forward(const moe_layer_desc* d, const moe_layer_weights* layers,
+                             int32_t n_layers, float* x, int32_t n_tokens, float* y_layers,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Test hook: dequantized weights of rows [row0, row0+n_rows) of one [rows][cols]
+ * matrix.  out_f32[r][c] = float(q) * scale[row], one fp32 multiply rounded to
+ * nearest even (for bf16 weights: the widened value).  out_bf16_codes
+ * (nullable, int formats only) receives bf16(q), exact for |q| <= 8. */
+moe_status moe_dequant_rows(int32_t dtype, const void* codes, const float* scales, int32_t cols,
+                            int32_t row0, int32_t n_rows, float* out_f32,
+                            uint16_t* out_bf16_codes, void* stream);
+
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */
