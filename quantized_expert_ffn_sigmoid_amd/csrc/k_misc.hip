@@ -1,0 +1,98 @@
+// k_misc.hip -- weighted combine of the routed experts plus the shared expert,
+// and the dequantization test hook (gfx950).
+#include "moe_internal.h"
+
+namespace moe {
+
+// out[t][o] = sum_j w[t][j] * Y[t*K + j][o] (j ascending) + S[t][o]
+// ("colibri" README, "What's implemented": routed_scaling_factor-weighted
+// combine with a shared expert; the scaling is already inside w).
+// With a residual: y_copy (optional) = the MoE output, out = residual + it.
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
+                                                 const float* __restrict__ topk_w,
+                                                 const float* __restrict__ S, int32_t K,
+                                                 int32_t H, const float* __restrict__ residual,
+                                                 float* __restrict__ out,
+                                                 float* __restrict__ y_copy) {
+  const int64_t t = blockIdx.y;
+  const int o = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (o >= H) return;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < K; ++j) {
+    const float w = topk_w[t * K + j];
+    const float4 y = *reinterpret_cast<const float4*>(Y + (t * K + j) * H + o);
+    acc.x = fmaf(w, y.x, acc.x);
+    acc.y = fmaf(w, y.y, acc.y);
+    acc.z = fmaf(w, y.z, acc.z);
+    acc.w = fmaf(w, y.w, acc.w);
+  }
+  if (S) {
+    const float4 sv = *reinterpret_cast<const float4*>(S + t * H + o);
+    acc.x += sv.x;
+    acc.y += sv.y;
+    acc.z += sv.z;
+    acc.w += sv.w;
+  }
+  if (residual) {
+    if (y_copy) *reinterpret_cast<float4*>(y_copy + t * H + o) = acc;
+    const float4 r = *reinterpret_cast<const float4*>(residual + t * H + o);
+    acc.x += r.x;
+    acc.y += r.y;
+    acc.z += r.z;
+    acc.w += r.w;
+  }
+  *reinterpret_cast<float4*>(out + t * H + o) = acc;
+}
+
+hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, int32_t T,
+                          int32_t K, int32_t H, const float* residual, float* out,
+                          float* y_copy, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const dim3 grid((H / 4 + 255) / 256, T);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, Y, topk_w, S, K, H, residual, out, y_copy);
+  return hipGetLastError();
+}
+
+// Dequantized weights: out[r][c] = float(q) * scale[row0 + r] (one rounded
+// fp32 multiply); out_bf16 = bf16 bits of q (exact for |q| <= 8).
+__global__ __launch_bounds__(256) void k_dequant(int dtype, const uint8_t* __restrict__ codes,
+                                                 const float* __restrict__ scales, int32_t cols,
+                                                 int32_t row0, int32_t n_rows,
+                                                 float* __restrict__ out,
+                                                 uint16_t* __restrict__ out_bf16) {
+  const int64_t n = (int64_t)n_rows * cols;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = row0 + i / cols;
+    const int64_t c = i % cols;
+    if (dtype == MOE_BF16) {
+      const uint16_t b = reinterpret_cast<const uint16_t*>(codes)[r * cols + c];
+      out[i] = bf16_bits_to_f32(b);
+      continue;
+    }
+    int q;
+    if (dtype == MOE_I4) {
+      const uint32_t v = (codes[r * (cols / 2) + c / 2] >> (4 * (c & 1))) & 0xFu;
+      q = (int)(v ^ 8u) - 8;
+    } else {
+      const uint32_t v = (codes[r * (cols / 4) + c / 4] >> (2 * (c & 3))) & 0x3u;
+      q = (int)(v ^ 2u) - 2;
+    }
+    out[i] = __fmul_rn((float)q, scales[r]);
+    if (out_bf16) out_bf16[i] = f32_to_bf16_bits((float)q);
+  }
+}
+
+hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
+                          int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
+                          hipStream_t s) {
+  const int64_t n = (int64_t)n_rows * cols;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)blocks), dim3(256), 0, s, dtype,
+                     reinterpret_cast<const uint8_t*>(codes), scales, cols, row0, n_rows, out,
+                     out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace moe

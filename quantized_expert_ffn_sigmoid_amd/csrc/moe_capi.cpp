@@ -1,0 +1,415 @@
+// moe_capi.cpp -- the C ABI of include/moe.h: host-side validation, workspace
+// carving and the launch sequence of the routed MoE layer on gfx950.
+//
+// No call allocates, frees or synchronises; every launch goes on the caller's
+// stream, so a decode step can be captured into a HIP graph by the caller.
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool dtype_is_weight(int32_t t) { return t == MOE_I4 || t == MOE_I2 || t == MOE_BF16; }
+
+// Descriptor consistency (MOE_EINVAL) and kernel coverage (MOE_EUNSUPPORTED).
+moe_status check_desc(const moe_layer_desc* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (d->top_k > d->n_experts) return MOE_EINVAL;
+  if (d->router != MOE_ROUTER_SIGMOID_NOAUX_TC && d->router != MOE_ROUTER_SOFTMAX_TOPK)
+    return MOE_EINVAL;
+  if (d->router == MOE_ROUTER_SIGMOID_NOAUX_TC) {
+    if (d->n_group <= 0 || d->n_experts % d->n_group != 0) return MOE_EINVAL;
+    if (d->topk_group <= 0 || d->topk_group > d->n_group) return MOE_EINVAL;
+    if ((int64_t)d->topk_group * (d->n_experts / d->n_group) < d->top_k) return MOE_EINVAL;
+  }
+  if (!dtype_is_weight(d->expert_dtype)) return MOE_EINVAL;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_EINVAL;
+  if (d->n_shared < 0 || d->n_shared > 1) return MOE_EINVAL;
+  if (d->n_shared > 0 && !dtype_is_weight(d->shared_dtype)) return MOE_EINVAL;
+  // kernel coverage
+  if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
+  if (d->router == MOE_ROUTER_SIGMOID_NOAUX_TC && d->n_group > 64) return MOE_EUNSUPPORTED;
+  if (d->hidden % 32 != 0) return MOE_EUNSUPPORTED;
+  if (!gemv_supported(d->expert_dtype, d->hidden) || !gemv_supported(d->expert_dtype, d->inter))
+    return MOE_EUNSUPPORTED;
+  if (d->n_shared > 0 && (!gemv_supported(d->shared_dtype, d->hidden) ||
+                          !gemv_supported(d->shared_dtype, d->inter * d->n_shared)))
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status check_set(const moe_expert_set* s, int32_t dtype) {
+  if (!s) return MOE_EINVAL;
+  if (!s->gate_up || !s->down || !aligned16(s->gate_up) || !aligned16(s->down)) return MOE_EINVAL;
+  if ((s->gate_up_stride & 15) || (s->down_stride & 15)) return MOE_EINVAL;
+  if (s->gate_up_stride < 0 || s->down_stride < 0) return MOE_EINVAL;
+  if (dtype != MOE_BF16) {
+    if (!s->gate_up_scale || !s->down_scale) return MOE_EINVAL;
+    if (!aligned16(s->gate_up_scale) || !aligned16(s->down_scale)) return MOE_EINVAL;
+    if ((s->gate_up_scale_stride & 15) || (s->down_scale_stride & 15)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+ExpertSetDev dev_set(const moe_expert_set& s) {
+  ExpertSetDev v;
+  v.gu = static_cast<const uint8_t*>(s.gate_up);
+  v.gu_stride = s.gate_up_stride;
+  v.gus = reinterpret_cast<const uint8_t*>(s.gate_up_scale);
+  v.gus_stride = s.gate_up_scale_stride;
+  v.dn = static_cast<const uint8_t*>(s.down);
+  v.dn_stride = s.down_stride;
+  v.dns = reinterpret_cast<const uint8_t*>(s.down_scale);
+  v.dns_stride = s.down_scale_stride;
+  return v;
+}
+
+// Workspace carve for n tokens.  Every region is 256-byte aligned.
+struct Carve {
+  size_t z, idx, w, counts, offsets, entries, inverse, active, n_active, h, h_sh, Y, S, xn, yl,
+      total;
+};
+
+Carve carve(const moe_layer_desc& d, int64_t T) {
+  Carve c{};
+  const int64_t E = d.n_experts, K = d.top_k, H = d.hidden, I = d.inter;
+  const int64_t Ish = (int64_t)d.inter * d.n_shared;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  c.z = take(sizeof(double) * T * E);
+  c.idx = take(sizeof(int32_t) * T * K);
+  c.w = take(sizeof(float) * T * K);
+  c.counts = take(sizeof(int32_t) * E);
+  c.offsets = take(sizeof(int32_t) * (E + 1));
+  c.entries = take(sizeof(int32_t) * T * K);
+  c.inverse = take(sizeof(int32_t) * T * K);
+  c.active = take(sizeof(int32_t) * E);
+  c.n_active = take(sizeof(int32_t));
+  c.h = take(sizeof(float) * T * K * I);
+  c.h_sh = take(sizeof(float) * T * (Ish > I ? Ish : I));
+  c.Y = take(sizeof(float) * T * K * H);
+  c.S = take(sizeof(float) * T * H);
+  c.xn = take(sizeof(float) * T * H);
+  c.yl = take(sizeof(float) * T * H);
+  c.total = o;
+  return c;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+void record(const moe_launch_opts* opts, int stage, int end, hipStream_t s) {
+  if (opts && opts->events) {
+    hipEvent_t ev = static_cast<hipEvent_t>(opts->events[2 * stage + end]);
+    if (ev) (void)hipEventRecord(ev, s);
+  }
+}
+
+#define MOE_TRY(expr)                       \
+  do {                                      \
+    if ((expr) != hipSuccess) return MOE_EHIP; \
+  } while (0)
+
+// The layer: out = combine(...) (+ residual when given; y_copy then receives
+// the layer output).  Arguments already validated.
+moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const void* x,
+                      int32_t T, float* out, int32_t* idx_out, float* w_out, void* ws,
+                      const float* residual, float* y_copy, hipStream_t s,
+                      const moe_launch_opts* opts) {
+  const Carve c = carve(d, T);
+  const int32_t E = d.n_experts, K = d.top_k, H = d.hidden, I = d.inter;
+  const int act_bf16 = d.act_dtype == MOE_BF16;
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(ws, c.idx);
+  float* tw = w_out ? w_out : at<float>(ws, c.w);
+  double* z = at<double>(ws, c.z);
+  int32_t* counts = at<int32_t>(ws, c.counts);
+  int32_t* offsets = at<int32_t>(ws, c.offsets);
+  int32_t* entries = at<int32_t>(ws, c.entries);
+  int32_t* inverse = at<int32_t>(ws, c.inverse);
+  int32_t* active = at<int32_t>(ws, c.active);
+  int32_t* n_active = at<int32_t>(ws, c.n_active);
+  void* h = at<void>(ws, c.h);
+  void* h_sh = at<void>(ws, c.h_sh);
+  float* Y = at<float>(ws, c.Y);
+  float* S = at<float>(ws, c.S);
+
+  record(opts, MOE_STAGE_ROUTE, 0, s);
+  MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, s));
+  MOE_TRY(launch_router_select(d, z, w.bias, T, idx, tw, s));
+  record(opts, MOE_STAGE_ROUTE, 1, s);
+
+  record(opts, MOE_STAGE_BUCKET, 0, s);
+  MOE_TRY(launch_bucket(T, K, E, idx, counts, offsets, entries, inverse, active, n_active, s));
+  record(opts, MOE_STAGE_BUCKET, 1, s);
+
+  RowSource routed{};
+  routed.routed = 1;
+  routed.active = active;
+  routed.n_active = n_active;
+  routed.offsets = offsets;
+  routed.entries = entries;
+  routed.top_k = K;
+  RowSource all{};
+  all.routed = 0;
+  all.fixed_expert = 0;
+  all.rows = nullptr;
+  all.n_rows = T;
+  all.row_div = 1;
+  const int max_slots = (int64_t)T * K < E ? T * K : E;
+
+  record(opts, MOE_STAGE_GATE_UP, 0, s);
+  GemvGateUpArgs gu{};
+  gu.w = dev_set(w.routed);
+  gu.H = H;
+  gu.I = I;
+  gu.x = x;
+  gu.h = h;
+  gu.src = routed;
+  MOE_TRY(launch_gemv_gate_up(gu, d.expert_dtype, act_bf16, max_slots, T, s));
+  if (d.n_shared > 0) {
+    GemvGateUpArgs gs = gu;
+    gs.w = dev_set(w.shared);
+    gs.I = I * d.n_shared;
+    gs.h = h_sh;
+    gs.src = all;
+    MOE_TRY(launch_gemv_gate_up(gs, d.shared_dtype, act_bf16, 1, T, s));
+  }
+  record(opts, MOE_STAGE_GATE_UP, 1, s);
+
+  record(opts, MOE_STAGE_DOWN, 0, s);
+  GemvDownArgs dn{};
+  dn.w = dev_set(w.routed);
+  dn.H = H;
+  dn.I = I;
+  dn.h = h;
+  dn.y = Y;
+  dn.src = routed;
+  MOE_TRY(launch_gemv_down(dn, d.expert_dtype, act_bf16, max_slots, T, s));
+  if (d.n_shared > 0) {
+    GemvDownArgs ds = dn;
+    ds.w = dev_set(w.shared);
+    ds.I = I * d.n_shared;
+    ds.h = h_sh;
+    ds.y = S;
+    ds.src = all;
+    MOE_TRY(launch_gemv_down(ds, d.shared_dtype, act_bf16, 1, T, s));
+  }
+  MOE_TRY(launch_combine(Y, tw, d.n_shared > 0 ? S : nullptr, T, K, H, residual, out, y_copy, s));
+  record(opts, MOE_STAGE_DOWN, 1, s);
+  return MOE_OK;
+}
+
+moe_status check_layer_args(const moe_layer_desc* d, const moe_layer_weights* w) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!w || !w->w_router || !aligned16(w->w_router)) return MOE_EINVAL;
+  if (w->bias && !aligned16(w->bias)) return MOE_EINVAL;
+  st = check_set(&w->routed, d->expert_dtype);
+  if (st != MOE_OK) return st;
+  if (d->n_shared > 0) {
+    st = check_set(&w->shared, d->shared_dtype);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens) {
+  if (check_desc(d) != MOE_OK || n_tokens < 0) return 0;
+  return carve(*d, n_tokens > 0 ? n_tokens : 1).total;
+}
+
+moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float* bias,
+                     const void* x, int32_t n_tokens, int32_t* topk_idx, float* topk_w, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_EINVAL;
+  if (n_tokens == 0) return MOE_OK;
+  if (!w_router || !x || !topk_idx || !topk_w || !ws) return MOE_EINVAL;
+  if (!aligned16(w_router) || !aligned16(x) || (bias && !aligned16(bias)) || !aligned16(ws))
+    return MOE_EINVAL;
+  if (ws_bytes < moe_workspace_bytes(d, n_tokens)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* z = at<double>(ws, carve(*d, n_tokens).z);
+  if (launch_router_logits(w_router, x, d->act_dtype == MOE_BF16, n_tokens, d->hidden,
+                           d->n_experts, z, s) != hipSuccess)
+    return MOE_EHIP;
+  if (launch_router_select(*d, z, bias, n_tokens, topk_idx, topk_w, s) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
+moe_status moe_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t* topk_idx,
+                      int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
+                      int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes,
+                      void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (n_tokens < 0 || top_k <= 0 || n_experts <= 0) return MOE_EINVAL;
+  if (n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (!counts || !offsets || !active || !n_active) return MOE_EINVAL;
+  if (n_tokens > 0 && (!topk_idx || !entries || !inverse)) return MOE_EINVAL;
+  if ((int64_t)n_tokens * top_k > INT32_MAX) return MOE_EUNSUPPORTED;
+  if (launch_bucket(n_tokens, top_k, n_experts, topk_idx, counts, offsets, entries, inverse,
+                    active, n_active, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, int32_t shared,
+                          int32_t expert, const void* x, const int32_t* rows, int32_t n_rows,
+                          int32_t row_div, float* y, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (n_rows < 0 || row_div <= 0) return MOE_EINVAL;
+  if (shared && (d->n_shared <= 0 || expert != 0)) return MOE_EINVAL;
+  if (!shared && (expert < 0 || expert >= d->n_experts)) return MOE_EINVAL;
+  if (n_rows == 0) return MOE_OK;
+  const int32_t dtype = shared ? d->shared_dtype : d->expert_dtype;
+  st = check_set(set, dtype);
+  if (st != MOE_OK) return st;
+  if (!x || !y || !ws || !aligned16(x) || !aligned16(y) || !aligned16(ws)) return MOE_EINVAL;
+  if (ws_bytes < moe_workspace_bytes(d, n_rows)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t I = shared ? d->inter * d->n_shared : d->inter;
+  const int act_bf16 = d->act_dtype == MOE_BF16;
+  void* h = at<void>(ws, carve(*d, n_rows).h);
+  RowSource src{};
+  src.routed = 0;
+  src.fixed_expert = expert;
+  src.rows = rows;
+  src.n_rows = n_rows;
+  src.row_div = row_div;
+  GemvGateUpArgs gu{};
+  gu.w = dev_set(*set);
+  gu.H = d->hidden;
+  gu.I = I;
+  gu.x = x;
+  gu.h = h;
+  gu.src = src;
+  if (launch_gemv_gate_up(gu, dtype, act_bf16, 1, n_rows, s) != hipSuccess) return MOE_EHIP;
+  RowSource hs = src;
+  hs.rows = nullptr;
+  hs.row_div = 1;
+  GemvDownArgs dn{};
+  dn.w = gu.w;
+  dn.H = d->hidden;
+  dn.I = I;
+  dn.h = h;
+  dn.y = y;
+  dn.src = hs;
+  if (launch_gemv_down(dn, dtype, act_bf16, 1, n_rows, s) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_layer_weights* w,
+                                const void* x, int32_t n_tokens, float* out,
+                                int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                size_t ws_bytes, void* stream, const moe_launch_opts* opts) {
+  moe_status st = check_layer_args(d, w);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_EINVAL;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !out || !ws || !aligned16(x) || !aligned16(out) || !aligned16(ws)) return MOE_EINVAL;
+  if (ws_bytes < moe_workspace_bytes(d, n_tokens)) return MOE_EWORKSPACE;
+  return layer_impl(*d, *w, x, n_tokens, out, topk_idx_out, topk_w_out, ws, nullptr, nullptr,
+                    static_cast<hipStream_t>(stream), opts);
+}
+
+moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
+                             int32_t n_tokens, float* out, int32_t* topk_idx_out,
+                             float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  return moe_layer_forward_ex(d, w, x, n_tokens, out, topk_idx_out, topk_w_out, ws, ws_bytes,
+                              stream, nullptr);
+}
+
+moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* out,
+                       void* stream) {
+  if (n_tokens < 0 || hidden <= 0 || !(eps >= 0.0f)) return MOE_EINVAL;
+  if (n_tokens == 0) return MOE_OK;
+  if (!x || !out) return MOE_EINVAL;
+  if (launch_rmsnorm(x, out, n_tokens, hidden, eps, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
+moe_status moe_stack_forward(const moe_layer_desc* d, const moe_layer_weights* layers,
+                             int32_t n_layers, float* x, int32_t n_tokens, float* y_layers,
+                             void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->act_dtype != MOE_F32) return MOE_EINVAL;
+  if (n_layers < 0 || n_tokens < 0 || !(d->norm_eps >= 0.0f)) return MOE_EINVAL;
+  if (n_layers == 0 || n_tokens == 0) return MOE_OK;
+  if (!layers || !x || !ws || !aligned16(x) || !aligned16(ws)) return MOE_EINVAL;
+  if (y_layers && !aligned16(y_layers)) return MOE_EINVAL;
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_layer_args(d, &layers[l]);
+    if (st != MOE_OK) return st;
+  }
+  if (ws_bytes < moe_workspace_bytes(d, n_tokens)) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Carve c = carve(*d, n_tokens);
+  float* xn = at<float>(ws, c.xn);
+  const int64_t TH = (int64_t)n_tokens * d->hidden;
+  for (int l = 0; l < n_layers; ++l) {
+    if (launch_rmsnorm(x, xn, n_tokens, d->hidden, d->norm_eps, s) != hipSuccess) return MOE_EHIP;
+    float* ycopy = y_layers ? y_layers + (int64_t)l * TH : nullptr;
+    st = layer_impl(*d, layers[l], xn, n_tokens, x, nullptr, nullptr, ws, x, ycopy, s, nullptr);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_dequant_rows(int32_t dtype, const void* codes, const float* scales, int32_t cols,
+                            int32_t row0, int32_t n_rows, float* out_f32,
+                            uint16_t* out_bf16_codes, void* stream) {
+  if (!dtype_is_weight(dtype)) return MOE_EINVAL;
+  if (cols <= 0 || row0 < 0 || n_rows < 0) return MOE_EINVAL;
+  if (n_rows == 0) return MOE_OK;
+  if (!codes || !out_f32) return MOE_EINVAL;
+  if (dtype != MOE_BF16 && !scales) return MOE_EINVAL;
+  if ((dtype == MOE_I4 && cols % 2) || (dtype == MOE_I2 && cols % 4)) return MOE_EUNSUPPORTED;
+  if (dtype == MOE_BF16 && out_bf16_codes) return MOE_EINVAL;
+  if (launch_dequant(dtype, codes, scales, cols, row0, n_rows, out_f32, out_bf16_codes,
+                     static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: shape or type outside the kernels' coverage";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+  }
+  return "unknown moe_status";
+}
+
+}  // extern "C"

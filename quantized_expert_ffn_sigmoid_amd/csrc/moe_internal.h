@@ -1,0 +1,114 @@
+// moe_internal.h -- device helpers and the launch interface between the C ABI
+// (moe_capi.cpp) and the gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kDecodeTokens = 16;   // router logits GEMV path handles up to this many tokens
+
+// ------------------------------------------------------------ device helpers
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------- launch structs
+
+// Device view of one expert set; all strides in bytes.
+struct ExpertSetDev {
+  const uint8_t* gu;
+  int64_t gu_stride;
+  const uint8_t* gus;
+  int64_t gus_stride;
+  const uint8_t* dn;
+  int64_t dn_stride;
+  const uint8_t* dns;
+  int64_t dns_stride;
+};
+
+// How a GEMV block finds its expert and rows.
+//  routed: slot = blockIdx.y -> expert active[slot] (slots >= n_active exit);
+//          bucket positions p in [offsets[e], offsets[e+1]); slot f = entries[p];
+//          token = f / top_k.
+//  list:   expert = fixed_expert; i in [0, n_rows); token = rows ? rows[i]/row_div : i.
+struct RowSource {
+  int routed;
+  const int32_t* active;
+  const int32_t* n_active;
+  const int32_t* offsets;
+  const int32_t* entries;
+  int32_t top_k;
+  int32_t fixed_expert;
+  const int32_t* rows;
+  int32_t n_rows;
+  int32_t row_div;
+};
+
+struct GemvGateUpArgs {
+  ExpertSetDev w;
+  int32_t H, I;            // I: this set's intermediate size
+  const void* x;           // [*][H], f32 or bf16 bits
+  void* h;                 // [rows][I], f32 or bf16 bits (act dtype)
+  RowSource src;
+};
+
+struct GemvDownArgs {
+  ExpertSetDev w;
+  int32_t H, I;
+  const void* h;           // [rows][I] act dtype
+  float* y;                // [rows][H] f32
+  RowSource src;
+};
+
+// ------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the
+// caller (moe_capi.cpp).
+
+hipError_t launch_rmsnorm(const float* x, float* out, int32_t T, int32_t H, float eps,
+                          hipStream_t s);
+hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
+                                int32_t H, int32_t E, double* z, hipStream_t s);
+hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const float* bias,
+                                int32_t T, int32_t* topk_idx, float* topk_w, hipStream_t s);
+hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_idx,
+                         int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
+                         int32_t* active, int32_t* n_active, hipStream_t s);
+// Gate/up + SwiGLU over the rows of `a.src`; `max_slots` = grid.y for routed mode.
+hipError_t launch_gemv_gate_up(const GemvGateUpArgs& a, int dtype, int act_bf16, int max_slots,
+                               int max_rows_per_slot, hipStream_t s);
+hipError_t launch_gemv_down(const GemvDownArgs& a, int dtype, int act_bf16, int max_slots,
+                            int max_rows_per_slot, hipStream_t s);
+// out[t] = sum_j w[t][j] * Y[t*k + j] + (S ? S[t] : 0) (+ residual[t] when given;
+// then y_copy[t] receives the MoE output without the residual).
+hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, int32_t T,
+                          int32_t K, int32_t H, const float* residual, float* out,
+                          float* y_copy, hipStream_t s);
+hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
+                          int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
+                          hipStream_t s);
+
+// Whether the GEMV kernels have an instantiation for a K (input length) of
+// this dtype: K / (elements per lane) must be a power of two <= 64.
+bool gemv_supported(int dtype, int32_t K);
+
+}  // namespace moe
