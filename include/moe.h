@@ -153,14 +153,17 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
                              float* topk_w_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Stage timing hook for moe_layer_forward_ex: when non-NULL, `events` is a
- * (host) array of 2*MOE_N_STAGES hipEvent_t handles; events[2s] is recorded on
- * `stream` right before stage s and events[2s+1] right after it. */
+ * (host) array of 2*MOE_N_STAGES hipEvent_t handles (entries may be NULL);
+ * events[2s] is recorded on `stream` right before the launches of stage s and
+ * events[2s+1] right after them.  While the stream is being captured into a
+ * graph the records are external event nodes, so each replay times the stage. */
 enum {
-  MOE_STAGE_ROUTE = 0,     /* router logits + selection                 */
-  MOE_STAGE_BUCKET = 1,    /* batch-union grouping                      */
-  MOE_STAGE_GATE_UP = 2,   /* expert gate/up + SwiGLU (routed + shared) */
-  MOE_STAGE_DOWN = 3,      /* expert down projections + combine         */
-  MOE_N_STAGES = 4
+  MOE_STAGE_ROUTE = 0,     /* router logits + selection (+ grouping, for <= 16 tokens) */
+  MOE_STAGE_BUCKET = 1,    /* batch-union grouping (empty when fused into ROUTE)      */
+  MOE_STAGE_GATE_UP = 2,   /* gate/up + SwiGLU of routed and shared experts, 1 launch */
+  MOE_STAGE_DOWN = 3,      /* down projections of routed and shared experts, 1 launch */
+  MOE_STAGE_COMBINE = 4,   /* weighted combine (+ residual in stacks)                 */
+  MOE_N_STAGES = 5
 };
 typedef struct {
   void* const* events;     /* (host) [2*MOE_N_STAGES] hipEvent_t, nullable */

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16, MOE_I4, MOE_I2 = 0, 1, 2, 3
 MOE_ROUTER_SIGMOID_NOAUX_TC, MOE_ROUTER_SOFTMAX_TOPK = 0, 1
-MOE_STAGE_ROUTE, MOE_STAGE_BUCKET, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_N_STAGES = 0, 1, 2, 3, 4
+(MOE_STAGE_ROUTE, MOE_STAGE_BUCKET, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE,
+ MOE_N_STAGES) = range(6)
 
 
 class MoeError(RuntimeError):

@@ -6,7 +6,7 @@
 // the selected indices are reproducible against an fp64 reference: two
 // orderings of an fp64 sum differ by ~1e-16 relative, far below the gaps
 // between distinct scores of continuous data.
-#include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -51,39 +51,59 @@ __device__ __forceinline__ float4 load_x4(const void* x, int act_bf16, int64_t o
   return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
 }
 
-// Decode shape (T <= 16): one wave per expert row; the row of W_r streams
-// through with 16-byte loads, tokens are re-read from L1/L2.
+// Decode shape (T <= 16): one block of 256 threads per expert row.  Each
+// thread requests its whole slice of the row (up to LG_QT 16-byte quads per
+// pass) before any arithmetic -- branch-free, with clamped addresses -- so a
+// row costs one memory round trip; the tokens then come from L1/L2.  Partial
+// sums are reduced in LDS along a fixed tree (deterministic fp64 order).
+constexpr int LG_QT = 8;
 __global__ __launch_bounds__(256) void k_logits_gemv(const float* __restrict__ W,
                                                      const void* __restrict__ x, int act_bf16,
                                                      int32_t T, int32_t H, int32_t E,
                                                      double* __restrict__ z) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+  __shared__ double red[kDecodeTokens][256];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const float* wr = W + (int64_t)e * H;
+  const int nq = H / 4;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
   double acc[kDecodeTokens];
 #pragma unroll
   for (int n = 0; n < kDecodeTokens; ++n) acc[n] = 0.0;
-  const float* wr = W + (int64_t)e * H;
-  for (int h = lane * 4; h < H; h += 256) {
-    const float4 w = *reinterpret_cast<const float4*>(wr + h);
+  for (int q0 = 0; q0 < nq; q0 += 256 * LG_QT) {
+    float4 w[LG_QT];
 #pragma unroll
-    for (int n = 0; n < kDecodeTokens; ++n) {
-      if (n < T) {
-        const float4 v = load_x4(x, act_bf16, (int64_t)n * H + h);
-        acc[n] = fma((double)w.x, (double)v.x, acc[n]);
-        acc[n] = fma((double)w.y, (double)v.y, acc[n]);
-        acc[n] = fma((double)w.z, (double)v.z, acc[n]);
-        acc[n] = fma((double)w.w, (double)v.w, acc[n]);
+    for (int i = 0; i < LG_QT; ++i) {
+      const int q = q0 + tid + 256 * i;
+      const float4 v = *reinterpret_cast<const float4*>(wr + 4 * (q < nq ? q : nq - 1));
+      w[i] = q < nq ? v : zero4;
+    }
+    for (int n = 0; n < T; ++n) {
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < LG_QT; ++i) {
+        const int q = q0 + tid + 256 * i;
+        float4 v = load_x4(x, act_bf16, (int64_t)n * H + 4 * (q < nq ? q : nq - 1));
+        if (q >= nq) v = zero4;
+        a = fma((double)w[i].x, (double)v.x, a);
+        a = fma((double)w[i].y, (double)v.y, a);
+        a = fma((double)w[i].z, (double)v.z, a);
+        a = fma((double)w[i].w, (double)v.w, a);
       }
+#pragma unroll
+      for (int m = 0; m < kDecodeTokens; ++m)
+        if (m == n) acc[m] += a;
     }
   }
 #pragma unroll
-  for (int n = 0; n < kDecodeTokens; ++n) {
-    if (n < T) {
-      const double v = wave_sum(acc[n]);
-      if (lane == 0) z[(int64_t)n * E + e] = v;
-    }
+  for (int n = 0; n < kDecodeTokens; ++n)
+    if (n < T) red[n][tid] = acc[n];
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st)
+      for (int n = 0; n < T; ++n) red[n][tid] += red[n][tid + st];
+    __syncthreads();
   }
+  if (tid < T) z[(int64_t)tid * E + e] = red[tid][0];
 }
 
 // Prefill shape: 64 tokens x 64 experts per block, fp64 FMA on LDS tiles.
@@ -151,8 +171,8 @@ hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf
                                 int32_t H, int32_t E, double* z, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (T <= kDecodeTokens) {
-    hipLaunchKernelGGL(k_logits_gemv, dim3((E + 3) / 4), dim3(256), 0, s, w_router, x, act_bf16,
-                       T, H, E, z);
+    hipLaunchKernelGGL(k_logits_gemv, dim3(E), dim3(256), 0, s, w_router, x, act_bf16, T, H, E,
+                       z);
   } else {
     dim3 grid((T + LG_BT - 1) / LG_BT, (E + LG_BE - 1) / LG_BE);
     hipLaunchKernelGGL(k_logits_gemm, grid, dim3(256), 0, s, w_router, x, act_bf16, T, H, E, z);
@@ -160,157 +180,35 @@ hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- selection
-// One wave per token.  Lane l holds experts l*EPL .. l*EPL+EPL-1 (contiguous,
-// so a group is a contiguous run of lanes' slots).  Every comparison prefers
-// the larger score and, on equal scores, the lower index.
-
-__device__ __forceinline__ bool beats(double va, int ia, double vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-// Wave-wide best (value, index); every lane receives the winner.
-__device__ __forceinline__ void wave_argbest(double& v, int& i) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const double ov = __shfl_xor(v, m, kWave);
-    const int oi = __shfl_xor(i, m, kWave);
-    if (beats(ov, oi, v, i)) {
-      v = ov;
-      i = oi;
-    }
-  }
-}
-
-// Wave-wide two largest values (a >= b); lanes hold their local (a, b).
-__device__ __forceinline__ void wave_top2(double& a, double& b) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const double oa = __shfl_xor(a, m, kWave);
-    const double ob = __shfl_xor(b, m, kWave);
-    const double hi = fmax(a, oa), lo = fmin(a, oa);
-    b = fmax(lo, fmax(b, ob));
-    a = hi;
-  }
-}
-
-struct SelectParams {
-  int32_t E, K, G, topk_group, softmax;
-  float scaling;
-};
-
 template <int EPL>
 __global__ __launch_bounds__(256) void k_select(SelectParams p, const double* __restrict__ z,
                                                 const float* __restrict__ bias, int32_t T,
                                                 int32_t* __restrict__ topk_idx,
                                                 float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const double NEG = -INFINITY;
-  const double* zt = z + (int64_t)t * p.E;
-  double c[EPL], sv[EPL];
-  bool open[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) {
-    const int e = lane * EPL + i;
-    const bool ok = e < p.E;
-    const double zv = ok ? zt[e] : 0.0;
-    if (p.softmax) {
-      sv[i] = zv;
-      c[i] = ok ? zv : NEG;
-    } else {
-      const double s = 1.0 / (1.0 + exp(-zv));
-      sv[i] = s;
-      c[i] = ok ? s + (bias ? (double)bias[e] : 0.0) : NEG;
-    }
-    open[i] = ok;
-  }
-
-  if (!p.softmax && p.topk_group < p.G) {
-    // group scores: sum of the two largest c in each contiguous group
-    const int per = p.E / p.G;
-    double my_gs = NEG;
-    for (int g = 0; g < p.G; ++g) {
-      double a = NEG, b = NEG;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane * EPL + i;
-        if (open[i] && e / per == g) {
-          if (c[i] > a) {
-            b = a;
-            a = c[i];
-          } else if (c[i] > b) {
-            b = c[i];
-          }
-        }
-      }
-      wave_top2(a, b);
-      if (lane == g) my_gs = (per == 1) ? a : a + b;
-    }
-    // keep the topk_group best groups
-    uint64_t kept = 0;
-    for (int r = 0; r < p.topk_group; ++r) {
-      double v = ((kept >> lane) & 1ull) ? NEG : my_gs;
-      int gi = lane < p.G && !((kept >> lane) & 1ull) ? lane : 0x7FFFFFFF;
-      if (lane >= p.G) v = NEG;
-      wave_argbest(v, gi);
-      kept |= 1ull << gi;
-    }
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane * EPL + i;
-      if (open[i] && !((kept >> (e / per)) & 1ull)) open[i] = false;
-    }
-  }
-
-  // top-k among open experts, in rank order
-  int my_idx = 0;
-  double my_s = 0.0, ssum = 0.0, z0 = 0.0;
-  for (int j = 0; j < p.K; ++j) {
-    double v = NEG;
-    int bi = 0x7FFFFFFF;
-    double bs = 0.0;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane * EPL + i;
-      if (open[i] && beats(c[i], e, v, bi)) {
-        v = c[i];
-        bi = e;
-        bs = sv[i];
-      }
-    }
-    // carry the winner's s along: reduce (v, bi), then fetch s from its owner
-    double rv = v;
-    int ri = bi;
-    wave_argbest(rv, ri);
-    const int owner = min(ri / EPL, kWave - 1);
-    const double s_win = __shfl(bs, owner, kWave);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane * EPL + i == ri) open[i] = false;
-    double contrib;
-    if (p.softmax) {
-      if (j == 0) z0 = s_win;
-      contrib = exp(s_win - z0);
-    } else {
-      contrib = s_win;
-    }
-    ssum += contrib;   // sequential sum in rank order
-    if (lane == j) {
-      my_idx = ri;
-      my_s = contrib;
-    }
-  }
-  if (lane < p.K) {
-    topk_idx[(int64_t)t * p.K + lane] = my_idx;
-    topk_w[(int64_t)t * p.K + lane] = (float)(my_s / ssum * (double)p.scaling);
-  }
+  select_token<EPL>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                    topk_w + (int64_t)t * p.K, nullptr);
 }
 
-hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const float* bias,
-                                int32_t T, int32_t* topk_idx, float* topk_w, hipStream_t s) {
-  if (T <= 0) return hipSuccess;
+// Decode: selection of all T <= 16 tokens (one wave each) and the grouping,
+// in one block of BK_THREADS threads.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_select_bucket(
+    SelectParams p, const double* __restrict__ z, const float* __restrict__ bias, int32_t T,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ int32_t s_idx[kDecodeTokens * kMaxTopK];
+  const int nw = blockDim.x >> 6;
+  for (int t = threadIdx.x >> 6; t < T; t += nw)
+    select_token<EPL>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                      topk_w + (int64_t)t * p.K, s_idx + t * p.K);
+  __syncthreads();
+  bucket_small(T, p.K, p.E, s_idx, counts, offsets, entries, inverse, active, n_active);
+}
+
+static SelectParams select_params(const moe_layer_desc& d) {
   SelectParams p;
   p.E = d.n_experts;
   p.K = d.top_k;
@@ -318,18 +216,41 @@ hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const 
   p.G = p.softmax ? 1 : d.n_group;
   p.topk_group = p.softmax ? 1 : d.topk_group;
   p.scaling = d.routed_scaling;
+  return p;
+}
+
+hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const float* bias,
+                                int32_t T, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const SelectParams p = select_params(d);
   const dim3 grid((T + 3) / 4), block(256);
   const int epl = (d.n_experts + 63) / 64;
-  if (epl <= 1)
-    hipLaunchKernelGGL(k_select<1>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w);
-  else if (epl <= 2)
-    hipLaunchKernelGGL(k_select<2>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w);
-  else if (epl <= 4)
-    hipLaunchKernelGGL(k_select<4>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w);
-  else if (epl <= 8)
-    hipLaunchKernelGGL(k_select<8>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w);
-  else
-    hipLaunchKernelGGL(k_select<16>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w);
+#define MOE_SEL(N) hipLaunchKernelGGL(k_select<N>, grid, block, 0, s, p, z, bias, T, topk_idx, topk_w)
+  if (epl <= 1) MOE_SEL(1);
+  else if (epl <= 2) MOE_SEL(2);
+  else if (epl <= 4) MOE_SEL(4);
+  else if (epl <= 8) MOE_SEL(8);
+  else MOE_SEL(16);
+#undef MOE_SEL
+  return hipGetLastError();
+}
+
+hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const float* bias,
+                                int32_t T, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* entries, int32_t* inverse,
+                                int32_t* active, int32_t* n_active, hipStream_t s) {
+  if (T <= 0 || T > kDecodeTokens) return hipErrorInvalidValue;
+  const SelectParams p = select_params(d);
+  const int epl = (d.n_experts + 63) / 64;
+#define MOE_SB(N)                                                                            \
+  hipLaunchKernelGGL(k_select_bucket<N>, dim3(1), dim3(256), 0, s, p, z, bias, T,            \
+                     topk_idx, topk_w, counts, offsets, entries, inverse, active, n_active)
+  if (epl <= 1) MOE_SB(1);
+  else if (epl <= 2) MOE_SB(2);
+  else if (epl <= 4) MOE_SB(4);
+  else if (epl <= 8) MOE_SB(8);
+  else MOE_SB(16);
+#undef MOE_SB
   return hipGetLastError();
 }
 

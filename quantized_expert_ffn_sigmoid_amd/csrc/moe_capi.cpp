@@ -45,8 +45,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->hidden % 32 != 0) return MOE_EUNSUPPORTED;
   if (!gemv_supported(d->expert_dtype, d->hidden) || !gemv_supported(d->expert_dtype, d->inter))
     return MOE_EUNSUPPORTED;
-  if (d->n_shared > 0 && (!gemv_supported(d->shared_dtype, d->hidden) ||
-                          !gemv_supported(d->shared_dtype, d->inter * d->n_shared)))
+  if (d->n_shared > 0 &&
+      (!gemv_pair_supported(d->expert_dtype, d->hidden, d->shared_dtype, d->hidden) ||
+       !gemv_pair_supported(d->expert_dtype, d->inter, d->shared_dtype, d->inter * d->n_shared)))
     return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -120,7 +121,12 @@ T* at(void* ws, size_t off) {
 void record(const moe_launch_opts* opts, int stage, int end, hipStream_t s) {
   if (opts && opts->events) {
     hipEvent_t ev = static_cast<hipEvent_t>(opts->events[2 * stage + end]);
-    if (ev) (void)hipEventRecord(ev, s);
+    if (!ev) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusActive)
+      (void)hipEventRecordWithFlags(ev, s, hipEventRecordExternal);
+    else
+      (void)hipEventRecord(ev, s);
   }
 }
 
@@ -154,67 +160,51 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
 
   record(opts, MOE_STAGE_ROUTE, 0, s);
   MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, s));
-  MOE_TRY(launch_router_select(d, z, w.bias, T, idx, tw, s));
+  const bool fused_route = T <= kDecodeTokens;
+  if (fused_route)
+    MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
+                                 active, n_active, s));
+  else
+    MOE_TRY(launch_router_select(d, z, w.bias, T, idx, tw, s));
   record(opts, MOE_STAGE_ROUTE, 1, s);
 
   record(opts, MOE_STAGE_BUCKET, 0, s);
-  MOE_TRY(launch_bucket(T, K, E, idx, counts, offsets, entries, inverse, active, n_active, s));
+  if (!fused_route)
+    MOE_TRY(launch_bucket(T, K, E, idx, counts, offsets, entries, inverse, active, n_active, s));
   record(opts, MOE_STAGE_BUCKET, 1, s);
 
-  RowSource routed{};
-  routed.routed = 1;
-  routed.active = active;
-  routed.n_active = n_active;
-  routed.offsets = offsets;
-  routed.entries = entries;
-  routed.top_k = K;
-  RowSource all{};
-  all.routed = 0;
-  all.fixed_expert = 0;
-  all.rows = nullptr;
-  all.n_rows = T;
-  all.row_div = 1;
-  const int max_slots = (int64_t)T * K < E ? T * K : E;
+  GemvArgs g{};
+  g.w = dev_set(w.routed);
+  if (d.n_shared > 0) g.ws = dev_set(w.shared);
+  g.src.routed = 1;
+  g.src.active = active;
+  g.src.n_active = n_active;
+  g.src.offsets = offsets;
+  g.src.entries = entries;
+  g.src.top_k = K;
+  g.has_shared = d.n_shared > 0;
+  g.n_tok = T;
+  g.H = H;
+  g.I = I;
+  g.Is = I * (d.n_shared > 0 ? d.n_shared : 1);
+  g.n_slots = (int64_t)T * K < E ? T * K : E;
+  g.x = x;
+  g.h = h;
+  g.h_s = h_sh;
+  g.y = Y;
+  g.y_s = S;
 
   record(opts, MOE_STAGE_GATE_UP, 0, s);
-  GemvGateUpArgs gu{};
-  gu.w = dev_set(w.routed);
-  gu.H = H;
-  gu.I = I;
-  gu.x = x;
-  gu.h = h;
-  gu.src = routed;
-  MOE_TRY(launch_gemv_gate_up(gu, d.expert_dtype, act_bf16, max_slots, T, s));
-  if (d.n_shared > 0) {
-    GemvGateUpArgs gs = gu;
-    gs.w = dev_set(w.shared);
-    gs.I = I * d.n_shared;
-    gs.h = h_sh;
-    gs.src = all;
-    MOE_TRY(launch_gemv_gate_up(gs, d.shared_dtype, act_bf16, 1, T, s));
-  }
+  MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_GATE_UP, 1, s);
 
   record(opts, MOE_STAGE_DOWN, 0, s);
-  GemvDownArgs dn{};
-  dn.w = dev_set(w.routed);
-  dn.H = H;
-  dn.I = I;
-  dn.h = h;
-  dn.y = Y;
-  dn.src = routed;
-  MOE_TRY(launch_gemv_down(dn, d.expert_dtype, act_bf16, max_slots, T, s));
-  if (d.n_shared > 0) {
-    GemvDownArgs ds = dn;
-    ds.w = dev_set(w.shared);
-    ds.I = I * d.n_shared;
-    ds.h = h_sh;
-    ds.y = S;
-    ds.src = all;
-    MOE_TRY(launch_gemv_down(ds, d.shared_dtype, act_bf16, 1, T, s));
-  }
-  MOE_TRY(launch_combine(Y, tw, d.n_shared > 0 ? S : nullptr, T, K, H, residual, out, y_copy, s));
+  MOE_TRY(launch_gemv(g, true, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_DOWN, 1, s);
+
+  record(opts, MOE_STAGE_COMBINE, 0, s);
+  MOE_TRY(launch_combine(Y, tw, d.n_shared > 0 ? S : nullptr, T, K, H, residual, out, y_copy, s));
+  record(opts, MOE_STAGE_COMBINE, 1, s);
   return MOE_OK;
 }
 
@@ -296,32 +286,25 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t I = shared ? d->inter * d->n_shared : d->inter;
   const int act_bf16 = d->act_dtype == MOE_BF16;
-  void* h = at<void>(ws, carve(*d, n_rows).h);
-  RowSource src{};
-  src.routed = 0;
-  src.fixed_expert = expert;
-  src.rows = rows;
-  src.n_rows = n_rows;
-  src.row_div = row_div;
-  GemvGateUpArgs gu{};
-  gu.w = dev_set(*set);
-  gu.H = d->hidden;
-  gu.I = I;
-  gu.x = x;
-  gu.h = h;
-  gu.src = src;
-  if (launch_gemv_gate_up(gu, dtype, act_bf16, 1, n_rows, s) != hipSuccess) return MOE_EHIP;
-  RowSource hs = src;
-  hs.rows = nullptr;
-  hs.row_div = 1;
-  GemvDownArgs dn{};
-  dn.w = gu.w;
-  dn.H = d->hidden;
-  dn.I = I;
-  dn.h = h;
-  dn.y = y;
-  dn.src = hs;
-  if (launch_gemv_down(dn, dtype, act_bf16, 1, n_rows, s) != hipSuccess) return MOE_EHIP;
+  GemvArgs g{};
+  g.w = dev_set(*set);
+  g.src.routed = 0;
+  g.src.fixed_expert = expert;
+  g.src.rows = rows;
+  g.src.n_rows = n_rows;
+  g.src.row_div = row_div;
+  g.has_shared = 0;
+  g.H = d->hidden;
+  g.I = I;
+  g.Is = I;
+  g.n_slots = 1;
+  g.x = x;
+  g.h = at<void>(ws, carve(*d, n_rows).h);
+  g.y = y;
+  if (launch_gemv(g, false, dtype, dtype, act_bf16, n_rows, s) != hipSuccess) return MOE_EHIP;
+  g.src.rows = nullptr;   // down reads h rows 0..n_rows-1 and writes y rows 0..n_rows-1
+  g.src.row_div = 1;
+  if (launch_gemv(g, true, dtype, dtype, act_bf16, n_rows, s) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }
 

@@ -47,7 +47,7 @@ struct ExpertSetDev {
 };
 
 // How a GEMV block finds its expert and rows.
-//  routed: slot = blockIdx.y -> expert active[slot] (slots >= n_active exit);
+//  routed: block slot -> expert active[slot] (slots >= n_active exit);
 //          bucket positions p in [offsets[e], offsets[e+1]); slot f = entries[p];
 //          token = f / top_k.
 //  list:   expert = fixed_expert; i in [0, n_rows); token = rows ? rows[i]/row_div : i.
@@ -64,20 +64,29 @@ struct RowSource {
   int32_t row_div;
 };
 
-struct GemvGateUpArgs {
-  ExpertSetDev w;
-  int32_t H, I;            // I: this set's intermediate size
-  const void* x;           // [*][H], f32 or bf16 bits
-  void* h;                 // [rows][I], f32 or bf16 bits (act dtype)
-  RowSource src;
+// GEMV geometry of one matrix for an input length K: a unit is kc K-chunks
+// of lpr lanes per row, rpp rows per unit (lpr * rpp = 64).
+struct MatGeo {
+  int32_t kc, lpr, rpp;
 };
 
-struct GemvDownArgs {
-  ExpertSetDev w;
-  int32_t H, I;
-  const void* h;           // [rows][I] act dtype
-  float* y;                // [rows][H] f32
+// One GEMV launch: the routed experts of a bucket (or a fixed expert over a
+// row list) and, optionally, the shared expert over tokens 0..n_tok-1.
+struct GemvArgs {
+  ExpertSetDev w;          // routed set (or the set of the fixed expert)
+  ExpertSetDev ws;         // shared set
   RowSource src;
+  int32_t has_shared, n_tok;
+  int32_t H, I, Is;        // Is: shared intermediate size
+  int32_t n_slots;         // routed slots in the grid
+  const void* x;           // gate/up input rows [*][H] (act dtype)
+  void* h;                 // routed h rows [bucket position][I] (act dtype)
+  void* h_s;               // shared h rows [token][Is]
+  float* y;                // routed down output rows [slot f][H]
+  float* y_s;              // shared down output rows [token][H]
+  // filled in by the launcher
+  MatGeo geo, geo_s;
+  int32_t rb, nb, rb_s;
 };
 
 // ------------------------------------------------------------- launchers
@@ -93,11 +102,18 @@ hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const 
 hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_idx,
                          int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
                          int32_t* active, int32_t* n_active, hipStream_t s);
-// Gate/up + SwiGLU over the rows of `a.src`; `max_slots` = grid.y for routed mode.
-hipError_t launch_gemv_gate_up(const GemvGateUpArgs& a, int dtype, int act_bf16, int max_slots,
-                               int max_rows_per_slot, hipStream_t s);
-hipError_t launch_gemv_down(const GemvDownArgs& a, int dtype, int act_bf16, int max_slots,
-                            int max_rows_per_slot, hipStream_t s);
+// Gate/up + SwiGLU (down = false) or the down projection (down = true) of
+// the routed slots and, when a.has_shared, the shared expert, in one launch.
+// max_rows_per_slot bounds the rows of any slot (1 selects the one-row path).
+hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
+                       int max_rows_per_slot, hipStream_t s);
+bool make_geo(int dtype, int32_t K, MatGeo& g);
+// Decode-sized routing: selection for T <= kDecodeTokens tokens and the
+// bucketing, in one single-block launch.
+hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const float* bias,
+                                int32_t T, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                                int32_t* offsets, int32_t* entries, int32_t* inverse,
+                                int32_t* active, int32_t* n_active, hipStream_t s);
 // out[t] = sum_j w[t][j] * Y[t*k + j] + (S ? S[t] : 0) (+ residual[t] when given;
 // then y_copy[t] receives the MoE output without the residual).
 hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, int32_t T,
@@ -107,8 +123,12 @@ hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);
 
-// Whether the GEMV kernels have an instantiation for a K (input length) of
-// this dtype: K / (elements per lane) must be a power of two <= 64.
+// Whether the GEMV kernels cover an input length K of this dtype: K must be
+// a whole number of 64-granule chunks, or a power-of-two number of granules
+// below 64 (granule: 32 int4/int2 codes or 8 bf16 values).
 bool gemv_supported(int dtype, int32_t K);
+// Whether a routed set (dtype, input K) and the shared set (sdtype, input Ks)
+// can share one launch: both covered, with the same per-lane slice geometry.
+bool gemv_pair_supported(int dtype, int32_t K, int sdtype, int32_t Ks);
 
 }  // namespace moe

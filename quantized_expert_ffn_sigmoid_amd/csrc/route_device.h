@@ -1,0 +1,403 @@
+// route_device.h -- device-side building blocks of the router selection and
+// of the batch-union grouping, shared by the routing kernels (gfx950).
+//
+// Selection ("colibri" README, "What's implemented": DeepSeek-V3-style sigmoid
+// router, noaux_tc, routed_scaling_factor): s = sigmoid(z), c = s + bias;
+// n_group contiguous groups scored by the sum of their two largest c; the
+// topk_group best groups kept; the top_k largest c among their experts chosen;
+// weights s / sum(s) * scaling.  Softmax top-k (Granite layer, "Glacial" page):
+// top_k largest z, weights softmax over them.  Every comparison prefers the
+// larger value and, on equal values, the lower index.
+#pragma once
+
+#include "moe_internal.h"
+
+namespace moe {
+
+__device__ __forceinline__ bool beats(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// ------------------------------------------------------- cross-lane moves
+// DPP lane moves (register to register, no LDS round trip).  All patterns
+// used here give every lane a valid source.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane j <-> 7-j within 8 lanes
+constexpr int kDppMirror = 0x140;     // lane j <-> 15-j within 16 lanes
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>((int)(b & 0xFFFFFFFFll));
+  const int hi = dpp_i<CTRL>((int)(b >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// One all-reduce step of (value, index) best-of with the partner of a move.
+template <int CTRL>
+__device__ __forceinline__ void argbest_step_dpp(double& v, int& i) {
+  const double ov = dpp_d<CTRL>(v);
+  const int oi = dpp_i<CTRL>(i);
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ void argbest_step_xor(double& v, int& i, int m) {
+  const double ov = __shfl_xor(v, m, kWave);
+  const int oi = __shfl_xor(i, m, kWave);
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide best (value, index); every lane receives the winner.
+__device__ __forceinline__ void wave_argbest(double& v, int& i) {
+  argbest_step_dpp<kDppXor1>(v, i);
+  argbest_step_dpp<kDppXor2>(v, i);
+  argbest_step_dpp<kDppHalfMirror>(v, i);
+  argbest_step_dpp<kDppMirror>(v, i);
+  argbest_step_xor(v, i, 16);
+  argbest_step_xor(v, i, 32);
+}
+
+// Two largest values (a >= b) merged with a partner's pair.
+__device__ __forceinline__ void top2_merge(double& a, double& b, double oa, double ob) {
+  const double hi = fmax(a, oa), lo = fmin(a, oa);
+  b = fmax(lo, fmax(b, ob));
+  a = hi;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void top2_step_dpp(double& a, double& b) {
+  top2_merge(a, b, dpp_d<CTRL>(a), dpp_d<CTRL>(b));
+}
+
+// Top-2 all-reduce within aligned segments of lpg lanes (lpg a power of 2).
+__device__ __forceinline__ void segment_top2(double& a, double& b, int lpg) {
+  if (lpg >= 2) top2_step_dpp<kDppXor1>(a, b);
+  if (lpg >= 4) top2_step_dpp<kDppXor2>(a, b);
+  if (lpg >= 8) top2_step_dpp<kDppHalfMirror>(a, b);
+  if (lpg >= 16) top2_step_dpp<kDppMirror>(a, b);
+  if (lpg >= 32) top2_merge(a, b, __shfl_xor(a, 16, kWave), __shfl_xor(b, 16, kWave));
+  if (lpg >= 64) top2_merge(a, b, __shfl_xor(a, 32, kWave), __shfl_xor(b, 32, kWave));
+}
+
+// Wave-wide two largest values (a >= b); lanes hold their local (a, b).
+__device__ __forceinline__ void wave_top2(double& a, double& b) { segment_top2(a, b, 64); }
+
+struct SelectParams {
+  int32_t E, K, G, topk_group, softmax;
+  float scaling;
+};
+
+// Selection for one token by one wave: zt = the token's E logits; writes its
+// k expert indices and weights (rank order) to idx_out / w_out, and the
+// indices also to idx_lds when given.  Lane l holds experts l*EPL ..
+// l*EPL+EPL-1, so a group is a run of consecutive lanes when EPL divides the
+// group size.
+template <int EPL>
+__device__ __forceinline__ void select_token(const SelectParams& p, const double* __restrict__ zt,
+                                             const float* __restrict__ bias, int32_t* idx_out,
+                                             float* w_out, int32_t* idx_lds) {
+  const int lane = threadIdx.x & 63;
+  const double NEG = -INFINITY;
+  double c[EPL], sv[EPL];
+  bool open[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    const bool ok = e < p.E;
+    const double zv = ok ? zt[e] : 0.0;
+    if (p.softmax) {
+      sv[i] = zv;
+      c[i] = ok ? zv : NEG;
+    } else {
+      const double s = 1.0 / (1.0 + exp(-zv));
+      sv[i] = s;
+      c[i] = ok ? s + (bias ? (double)bias[e] : 0.0) : NEG;
+    }
+    open[i] = ok;
+  }
+
+  if (!p.softmax && p.topk_group < p.G) {
+    const int per = p.E / p.G;
+    const int lpg = per / EPL;
+    const bool seg = per % EPL == 0 && lpg >= 1 && lpg <= kWave && (lpg & (lpg - 1)) == 0;
+    if (seg) {
+      // every lane's experts lie in one group: segmented top-2, then rank the
+      // groups against each other through scalar broadcasts
+      double a = NEG, b = NEG;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if (!open[i]) continue;
+        if (c[i] > a) {
+          b = a;
+          a = c[i];
+        } else if (c[i] > b) {
+          b = c[i];
+        }
+      }
+      segment_top2(a, b, lpg);
+      const double gs = per == 1 ? a : a + b;
+      const int my_g = (lane * EPL) / per;
+      int rank = 0;
+      for (int g = 0; g < p.G; ++g) {
+        const double sg = readlane_d(gs, g * lpg);
+        rank += beats(sg, g, gs, my_g) ? 1 : 0;
+      }
+      if (rank >= p.topk_group) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) open[i] = false;
+      }
+    } else {
+      // general shapes: one group at a time
+      double my_gs = NEG;
+      for (int g = 0; g < p.G; ++g) {
+        double a = NEG, b = NEG;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          const int e = lane * EPL + i;
+          if (open[i] && e / per == g) {
+            if (c[i] > a) {
+              b = a;
+              a = c[i];
+            } else if (c[i] > b) {
+              b = c[i];
+            }
+          }
+        }
+        wave_top2(a, b);
+        if (lane == g) my_gs = (per == 1) ? a : a + b;
+      }
+      uint64_t kept = 0;
+      for (int r = 0; r < p.topk_group; ++r) {
+        const bool live = lane < p.G && !((kept >> lane) & 1ull);
+        double v = live ? my_gs : NEG;
+        int gi = live ? lane : 0x7FFFFFFF;
+        wave_argbest(v, gi);
+        kept |= 1ull << gi;
+      }
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane * EPL + i;
+        if (open[i] && !((kept >> (e / per)) & 1ull)) open[i] = false;
+      }
+    }
+  }
+
+  // top-k among the open experts, in rank order
+  int my_idx = 0;
+  double my_s = 0.0, ssum = 0.0, z0 = 0.0;
+  for (int j = 0; j < p.K; ++j) {
+    double v = NEG;
+    int bi = 0x7FFFFFFF;
+    double bs = 0.0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane * EPL + i;
+      if (open[i] && beats(c[i], e, v, bi)) {
+        v = c[i];
+        bi = e;
+        bs = sv[i];
+      }
+    }
+    double rv = v;
+    int ri = bi;
+    wave_argbest(rv, ri);
+    const int owner = min(ri / EPL, kWave - 1);
+    const double s_win = readlane_d(bs, owner);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane * EPL + i == ri) open[i] = false;
+    double contrib;
+    if (p.softmax) {
+      if (j == 0) z0 = s_win;
+      contrib = exp(s_win - z0);
+    } else {
+      contrib = s_win;
+    }
+    ssum += contrib;   // sequential sum in rank order
+    if (lane == j) {
+      my_idx = ri;
+      my_s = contrib;
+    }
+  }
+  if (lane < p.K) {
+    idx_out[lane] = my_idx;
+    w_out[lane] = (float)(my_s / ssum * (double)p.scaling);
+    if (idx_lds) idx_lds[lane] = my_idx;
+  }
+}
+
+// -------------------------------------------------------------- grouping
+// Batch-union grouping ("colibri" README, "What's implemented"): a stable
+// counting sort of the flat slots f = t*k + j by expert, in one block of
+// BK_THREADS threads.  idx may point to global memory or to LDS.
+
+constexpr int BK_THREADS = 1024;
+constexpr int BK_WAVES = BK_THREADS / kWave;
+constexpr int BK_KEY_BITS = 10;   // experts < 1024
+constexpr int BK_SMALL = 512;     // slot counts up to this take the direct path
+
+// Small slot counts (F <= BK_SMALL): a slot's position is (slots of smaller
+// experts) + (earlier slots of the same expert); every expert counts its
+// slots itself.  Any block size.
+__device__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx,
+                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
+                             int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ int s_key[BK_SMALL];
+  __shared__ int s_rank[BK_SMALL];
+  __shared__ int s_off[kMaxExperts];
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int F = T * K;
+  for (int f = tid; f < F; f += nth) {
+    const int e = idx[f];
+    s_key[f] = (e >= 0 && e < E) ? e : -1;
+  }
+  __syncthreads();
+  for (int f = tid; f < F; f += nth) {
+    const int key = s_key[f];
+    int r = 0;
+    for (int g = 0; g < f; ++g) r += s_key[g] == key ? 1 : 0;
+    s_rank[f] = r;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += nth) {
+    int off = 0, cnt = 0, before = 0;
+    for (int f = 0; f < F; ++f) {
+      const int key = s_key[f];
+      if (key < 0) continue;
+      off += key < e ? 1 : 0;
+      cnt += key == e ? 1 : 0;
+      before += (key < e && s_rank[f] == 0) ? 1 : 0;
+    }
+    counts[e] = cnt;
+    offsets[e] = off;
+    s_off[e] = off;
+    if (cnt) active[before] = e;
+  }
+  if (tid == 0) {
+    int tot = 0, distinct = 0;
+    for (int f = 0; f < F; ++f) {
+      tot += s_key[f] >= 0 ? 1 : 0;
+      distinct += (s_key[f] >= 0 && s_rank[f] == 0) ? 1 : 0;
+    }
+    offsets[E] = tot;
+    n_active[0] = distinct;
+  }
+  __syncthreads();
+  for (int f = tid; f < F; f += nth) {
+    const int key = s_key[f];
+    if (key < 0) continue;
+    const int pos = s_off[key] + s_rank[f];
+    entries[pos] = f;
+    inverse[f] = pos;
+  }
+}
+
+__device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx,
+                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
+                             int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+  __shared__ int s_cnt[kMaxExperts];
+  __shared__ int s_base[kMaxExperts];
+  __shared__ int s_wcnt[BK_WAVES][kMaxExperts];
+  __shared__ int s_scan[BK_THREADS];
+  __shared__ int s_flag[BK_THREADS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t F = (int64_t)T * K;
+
+  // General path: LDS histogram, exclusive scan, scatter in rounds.
+  for (int e = tid; e < E; e += BK_THREADS) {
+    s_cnt[e] = 0;
+    for (int w = 0; w < BK_WAVES; ++w) s_wcnt[w][e] = 0;
+  }
+  __syncthreads();
+  for (int64_t f = tid; f < F; f += BK_THREADS) {
+    const int e = idx[f];
+    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+
+  // exclusive scans of the counts and of the nonzero flags (E <= 1024 = one
+  // element per thread), Hillis-Steele in LDS
+  const int v = tid < E ? s_cnt[tid] : 0;
+  const int fl = v > 0 ? 1 : 0;
+  s_scan[tid] = v;
+  s_flag[tid] = fl;
+  __syncthreads();
+  for (int d = 1; d < BK_THREADS; d <<= 1) {
+    const int a = tid >= d ? s_scan[tid - d] : 0;
+    const int b = tid >= d ? s_flag[tid - d] : 0;
+    __syncthreads();
+    s_scan[tid] += a;
+    s_flag[tid] += b;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int excl = s_scan[tid] - v;
+    counts[tid] = v;
+    offsets[tid] = excl;
+    s_base[tid] = excl;
+    if (fl) active[s_flag[tid] - 1] = tid;
+  }
+  if (tid == 0) {
+    offsets[E] = s_scan[E - 1];
+    n_active[0] = s_flag[E - 1];
+  }
+  __syncthreads();
+
+  // Within a round of BK_THREADS slots, a slot's rank among equal experts
+  // comes from ten ballots over the expert id's bits (the mask of lanes with
+  // the same expert) and per-wave counts in LDS for earlier waves: no atomics
+  // on positions, so the order is the stable one.
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t r0 = 0; r0 < F; r0 += BK_THREADS) {
+    const int64_t f = r0 + tid;
+    const int e = f < F ? idx[f] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < BK_KEY_BITS; ++b) {
+      const bool bit = valid && ((e >> b) & 1);
+      const uint64_t bm = __ballot(bit);
+      m &= bit ? bm : ~bm;
+    }
+    const int rank = __popcll(m & lt_mask);
+    const int cnt = __popcll(m);
+    const bool leader = valid && rank == 0;
+    if (leader) s_wcnt[wave][e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = s_base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
+      entries[pos] = (int32_t)f;
+      inverse[f] = pos;
+    }
+    __syncthreads();
+    if (leader) {
+      atomicAdd(&s_base[e], cnt);
+      s_wcnt[wave][e] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace moe
