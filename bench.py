@@ -13,9 +13,10 @@ each step reads its experts, shared expert and router from HBM rather than
 from the 256 MB Infinity Cache, as successive layers of a decoder would.
 
 The timed steps are captured once into a HIP graph and replayed (the library
-allocates nothing and never synchronises, so the whole step is capturable);
-an event pair around the routed gate/up launch of every step times the
-dominant kernel inside the same replay.
+allocates nothing and never synchronises, so the whole step is capturable).
+A second replay of the same steps carries an event pair around the gate/up
+launch of every step (and around every stage with --stages): it times the
+dominant kernel without putting event nodes into the headline loop.
 
 Output: one JSON line (see the fields below).  --gpus N > 1 exits: this
 build runs on one GPU.
@@ -235,27 +236,35 @@ def main():
         capi.moe_layer_forward_ex(desc, weights[l], xs[p], T, out, None, None, ws, nb,
                                   stream=stream.cuda_stream, events=events)
 
+    # The headline loop carries no event nodes; per-kernel durations come from a
+    # second pass over the same K steps with events around the stages.
     if args.eager:
         for i in range(W):
             step(i, False)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(K):
-            step(i, True)
+            step(i, False)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        for i in range(K):
+            step(i, True)
+        torch.cuda.synchronize()
     else:
         sh = stream.cuda_stream
         step(0, False)                       # first launches outside any capture
         torch.cuda.synchronize()
         gw = hip.capture(sh, lambda: [step(i, False) for i in range(W)])
-        gt = hip.capture(sh, lambda: [step(i, True) for i in range(K)])
+        gt = hip.capture(sh, lambda: [step(i, False) for i in range(K)])
+        ge = hip.capture(sh, lambda: [step(i, True) for i in range(K)])
         hip.launch(gw, sh)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         hip.launch(gt, sh)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        hip.launch(ge, sh)
+        torch.cuda.synchronize()
 
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / K

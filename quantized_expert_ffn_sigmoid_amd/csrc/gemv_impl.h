@@ -9,21 +9,20 @@
 // in flight, and a short unpack -- not around matrix cores.
 //
 // Work decomposition.  A matrix row is cut into granules of 16 bytes (8 for
-// int2).  A "unit" is one K-chunk of 64 granules of one row (of a gate/up row
-// pair for the gate/up kernel): the 64 lanes of a wave load it as one 1 KB
-// contiguous read.  Rows shorter than 64 granules put several rows in one
-// unit (lanes-per-row LPR < 64).  A block owns a range of rows of one matrix
-// and deals its units round-robin to its waves; each wave issues the loads of
-// its next unit before computing the current one.  Activation rows are staged
-// once per block in LDS in a lane-major layout (each ds_read_b128 of a wave
-// touches 64 consecutive 16-byte slots, no bank conflicts).  Per-unit partial
-// sums are reduced across the unit's lanes with shuffles and across K-chunks
-// in LDS; the epilogue applies the per-row scale (constant along a row, so it
-// commutes with the K-sum), SwiGLU, and writes h or y.
+// int2); the lpr lanes of a lane group (64, or fewer for short rows) share a
+// row, lane j taking granules j, j + lpr, j + 2 lpr, ...  so that each load
+// instruction of a wave reads whole 1 KB runs.  A lane keeps the activation
+// values of its granule positions (its K-slice, KSL = K / lpr elements) in
+// registers for the whole block, and the block's waves stream disjoint rows
+// of one matrix (row pairs gate/up for the gate/up kernel) with several steps
+// of loads in flight.  A row's partial dot products are summed over its lane
+// group with DPP moves; the epilogue applies the per-row scale (constant along
+// a row, so it commutes with the K-sum), SwiGLU, and writes h or y.
 //
-// Codes are unpacked as offset-binary bytes: XOR of the sign bits, two masks,
-// then the byte-to-float conversions; the offset times the lane's activation
-// sum is removed once per unit.  Accumulation is fp32 throughout.
+// Codes are unpacked as offset-binary bytes: an XOR of the sign bits, two
+// masks, then packed conversions of byte pairs; the offset times the
+// activation sum of the granule is removed once per granule.  Accumulation is
+// fp32 throughout.
 #pragma once
 
 #include "moe_internal.h"
@@ -32,31 +31,29 @@ namespace moe {
 
 template <int WDT>
 struct Fmt;
+// EPG: elements per granule, GB: granule bytes, DW: granule dwords.  The int
+// formats unpack a code c (offset-binary, c = q + OFF) to c * UNIT: a byte
+// 0..15 read as an OCP e4m3 float is exactly b * 2^-9 (subnormals, then the
+// first binade), so one packed conversion yields two codes.
 template <>
 struct Fmt<MOE_I4> {
   static constexpr int EPG = 32, GB = 16, DW = 4;
-  static constexpr float OFF = 8.0f;
+  static constexpr float OFF = 8.0f, UNIT = 1.0f / 512.0f;
 };
 template <>
 struct Fmt<MOE_I2> {
   static constexpr int EPG = 32, GB = 8, DW = 2;
-  static constexpr float OFF = 2.0f;
+  static constexpr float OFF = 2.0f, UNIT = 1.0f / 512.0f;
 };
 template <>
 struct Fmt<MOE_BF16> {
   static constexpr int EPG = 8, GB = 16, DW = 4;
-  static constexpr float OFF = 0.0f;
+  static constexpr float OFF = 0.0f, UNIT = 1.0f;
 };
-
-// Keeps the optimiser from folding the byte masks into 4-bit field extracts,
-// so that each code converts with one v_cvt_f32_ubyteN.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Codes are streamed once: non-temporal loads keep them from displacing the
 // activations and router weights in the caches.
@@ -86,17 +83,22 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
   if constexpr (WDT == MOE_I4) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
+      // offset-binary nibbles, even ones in lo's bytes, odd ones in hi's
       const uint32_t w = gr[d] ^ 0x88888888u;
-      const uint32_t lo = opaque(w & 0x0F0F0F0Fu);
-      const uint32_t hi = opaque((w >> 4) & 0x0F0F0F0Fu);
+      const uint32_t lo = w & 0x0F0F0F0Fu;
+      const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+      const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
+      const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+      const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+      const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+      const float ql[4] = {l01.x, l01.y, l23.x, l23.y};
+      const float qh[4] = {h01.x, h01.y, h23.x, h23.y};
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const float ql = (float)((lo >> (8 * b)) & 0xFFu);
-        const float qh = (float)((hi >> (8 * b)) & 0xFFu);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          acc[n] = fmaf(ql, x[n][b0 + 8 * d + 2 * b], acc[n]);
-          acc[n] = fmaf(qh, x[n][b0 + 8 * d + 2 * b + 1], acc[n]);
+          acc[n] = fmaf(ql[b], x[n][b0 + 8 * d + 2 * b], acc[n]);
+          acc[n] = fmaf(qh[b], x[n][b0 + 8 * d + 2 * b + 1], acc[n]);
         }
       }
     }
@@ -106,12 +108,14 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
       const uint32_t w = gr[d] ^ 0xAAAAAAAAu;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t c = opaque((w >> (2 * jj)) & 0x03030303u);
+        const uint32_t c = (w >> (2 * jj)) & 0x03030303u;
+        const f32x2 c01 = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+        const f32x2 c23 = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+        const float q[4] = {c01.x, c01.y, c23.x, c23.y};
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const float q = (float)((c >> (8 * b)) & 0xFFu);
 #pragma unroll
-          for (int n = 0; n < NT; ++n) acc[n] = fmaf(q, x[n][b0 + 16 * d + 4 * b + jj], acc[n]);
+          for (int n = 0; n < NT; ++n) acc[n] = fmaf(q[b], x[n][b0 + 16 * d + 4 * b + jj], acc[n]);
         }
       }
     }
@@ -296,7 +300,7 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
                 if constexpr (WDT != MOE_BF16) {
 #pragma unroll
                   for (int n = 0; n < NT; ++n)
-                    acc[m][n] = fmaf(-F::OFF, gs[n][s2 * CG + g], acc[m][n]);
+                    acc[m][n] = fmaf(-F::OFF * F::UNIT, gs[n][s2 * CG + g], acc[m][n]);
                 }
               }
           }
@@ -316,8 +320,8 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
           if (ok) {
             float sa = 1.f, sb = 1.f;
             if constexpr (WDT != MOE_BF16) {
-              sa = scale[0];
-              if constexpr (PAIR) sb = scale[NM - 1];
+              sa = scale[0] * (1.0f / F::UNIT);
+              if constexpr (PAIR) sb = scale[NM - 1] * (1.0f / F::UNIT);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
@@ -341,19 +345,261 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
   }
 }
 
-// Which matrix and which token rows a block handles.
+// ------------------------------------------------------------ ring path
+// Rows of at least 64 granules (all 64 lanes of a wave on one row, so every
+// wave load is one contiguous 1 KB run): the codes stream through a per-wave
+// ring of kRing 1 KB LDS slots filled by direct global-to-LDS loads.  Loads
+// in flight then hold no registers, and a slot is refilled as soon as its
+// data has been consumed, so about kRing KB per wave stay in flight.
+// Completion is tracked with explicit vmcnt waits.  Inside the loop the only
+// vector memory instructions are the ring loads (row results go to LDS and
+// are written at the end of the block; row scales are staged in LDS first),
+// and loads complete in issue order, so "slot n has landed" is "no more than
+// the number of younger ring loads are pending".
+constexpr int kRing = 16;
+constexpr int kMaxRingRows = 512;   // rows per block on the ring path
+
+struct RingLds {
+  uint8_t ring[kWaves][kRing][1024];
+  float out[2][kMaxRingRows];     // per token of the chunk
+  float scale[2][kMaxRingRows];   // gate (or the only matrix), up
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Activation slices through LDS: the block copies the nt activation rows into
+// LDS with coalesced 16-byte loads (all blocks read the same few rows, so
+// per-lane strided loads would flood the L2 with requests), then every lane
+// reads its granules' activations.  Chunk q -- the EPG activations of granule
+// q -- sits at q * (CB + 16) bytes; the padding puts the 16-byte reads of 16
+// consecutive lanes on distinct banks.  Ends with a barrier, after which the
+// staging area may be reused.
+template <int EPG, int KSL, int NT, int ABF16>
+__device__ __forceinline__ void slices_via_lds(const void* src, const int64_t* xoff, int nt, int K,
+                                               uint8_t* stage, float (&x)[NT][KSL],
+                                               float (&gs)[NT][KSL / EPG]) {
+  constexpr int AB = ABF16 ? 2 : 4, CB = EPG * AB, CS = CB + 16, PPC = CB / 16;
+  constexpr int GPL = KSL / EPG;
+  static_assert(NT * (KSL * 64 / EPG) * CS <= kWaves * kRing * 1024, "staging fits the ring area");
+  const int rowb = (K / EPG) * CS;
+  const int pieces = K * AB / 16;
+  for (int n = 0; n < nt && n < NT; ++n) {
+    const uint8_t* g = reinterpret_cast<const uint8_t*>(src) + xoff[n] * AB;
+    for (int p = threadIdx.x; p < pieces; p += kThreads) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(g + (int64_t)p * 16);
+      const int q = p / PPC, r = p - q * PPC;
+      *reinterpret_cast<u32x4*>(stage + n * rowb + q * CS + r * 16) = v;
+    }
+  }
+  __syncthreads();
+  const int j = threadIdx.x & 63;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint8_t* row = stage + (n < nt ? n : 0) * rowb;
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      const uint8_t* c = row + (g * 64 + j) * CS;
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < PPC; ++r) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(c + r * 16);
+        if constexpr (ABF16) {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float lo = __uint_as_float(w[d] << 16), hi = __uint_as_float(w[d] & 0xFFFF0000u);
+            x[n][g * EPG + r * 8 + 2 * d] = lo;
+            x[n][g * EPG + r * 8 + 2 * d + 1] = hi;
+            s += lo + hi;
+          }
+        } else {
+          const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                              __uint_as_float(v.w)};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) x[n][g * EPG + r * 4 + d] = f[d];
+          s += (f[0] + f[1]) + (f[2] + f[3]);
+        }
+      }
+      gs[n][g] = s;
+    }
+  }
+  __syncthreads();
+}
+
+// Activation slices read straight from rows in the sliced layout: lane j's
+// piece c of granule g is the 16 bytes at ((g * PPC + c) * 64 + j) * 16, so
+// every load instruction of the wave reads one contiguous 1 KB run.
+template <int EPG, int KSL, int NT, int ABF16>
+__device__ __forceinline__ void slices_sliced(const void* src, const int64_t* xoff, int nt,
+                                              float (&x)[NT][KSL], float (&gs)[NT][KSL / EPG]) {
+  constexpr int AB = ABF16 ? 2 : 4, P = 16 / AB, PPC = EPG / P, GPL = KSL / EPG;
+  const int j = threadIdx.x & 63;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(src) + xoff[n < nt ? n : 0] * AB;
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < PPC; ++c) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + ((int64_t)(g * PPC + c) * 64 + j) * 16);
+        if constexpr (ABF16) {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const float lo = __uint_as_float(w[d] << 16), hi = __uint_as_float(w[d] & 0xFFFF0000u);
+            x[n][g * EPG + c * 8 + 2 * d] = lo;
+            x[n][g * EPG + c * 8 + 2 * d + 1] = hi;
+            s += lo + hi;
+          }
+        } else {
+          const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                              __uint_as_float(v.w)};
+#pragma unroll
+          for (int d = 0; d < 4; ++d) x[n][g * EPG + c * 4 + d] = f[d];
+          s += (f[0] + f[1]) + (f[2] + f[3]);
+        }
+      }
+      gs[n][g] = s;
+    }
+  }
+}
+
+// The wave's rows of the block: local rows wave, wave + kWaves, ... < nr.
+// Row results (scaled, SwiGLU applied for PAIR) go to L.out[n][local row].
+// With sliced input rows the weight loads are issued first, so that their
+// latency covers the activation loads and the scale staging; otherwise the
+// activation rows are staged through the ring area before the ring starts.
+// stage_scales: copy the block's row scales to L.scale (first chunk of a
+// block); every wave of the block calls this together.
+template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED>
+__device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff, int nt,
+                         bool stage_scales, RingLds& L) {
+  using F = Fmt<WDT>;
+  constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
+  constexpr int NM = PAIR ? 2 : 1, S = NM * GPL;
+  static_assert(GB == 16, "ring slots hold 16-byte granules");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rbytes = (int64_t)(jb.K / EPG) * GB;
+
+  float x[NT][KSL], gs[NT][GPL];
+  if constexpr (!SLICED) slices_via_lds<EPG, KSL, NT, ABF16>(src, xoff, nt, jb.K, &L.ring[0][0][0], x, gs);
+
+  const int my_rows = wave < nr ? (nr - wave + kWaves - 1) / kWaves : 0;
+  const int total = my_rows * S;
+  uint8_t* ring = &L.ring[wave][0][0];
+  const uint8_t* lane_base = jb.W + (int64_t)jb.r0 * rbytes + lane * GB;
+  // slot n of the stream: local row i = n / S, matrix m, granule g
+  auto issue = [&](int n) {
+    const int i = n / S, idx = n - i * S;
+    const int m = idx / GPL, g = idx - m * GPL;
+    const int64_t row = wave + i * kWaves + m * jb.rows;
+    const uint8_t* p = lane_base + row * rbytes + g * (64 * GB);
+    __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(ring + (n & (kRing - 1)) * 1024), 16, 0, 0);
+  };
+  const int pro = total < kRing ? total : kRing;
+  for (int n = 0; n < pro; ++n) issue(n);
+
+  if (stage_scales && WDT != MOE_BF16) {
+    for (int t = threadIdx.x; t < nr; t += kThreads) {
+      L.scale[0][t] = jb.S[jb.r0 + t];
+      if (PAIR) L.scale[1][t] = jb.S[jb.rows + jb.r0 + t];
+    }
+    __syncthreads();
+  }
+  if constexpr (SLICED) slices_sliced<EPG, KSL, NT, ABF16>(src, xoff, nt, x, gs);
+
+  auto read_slot = [&](int n) {
+    return *reinterpret_cast<const u32x4*>(ring + (n & (kRing - 1)) * 1024 + lane * 16);
+  };
+  // slot sn + 1 is read while slot sn is computed; before its read, the loads
+  // younger than it are ring refills (and, early on, the activation and scale
+  // loads, which only make the count conservative), at most kRing - 2 of them
+  u32x4 vnext = {0u, 0u, 0u, 0u};
+  if (total > 0) {
+    if (total - 1 >= kRing - 2) wait_vmcnt<kRing - 2>();
+    else wait_vmcnt<0>();
+    vnext = read_slot(0);
+  }
+
+  for (int i = 0; i < my_rows; ++i) {
+    float acc[NM][NT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[m][n] = 0.f;
+#pragma unroll
+    for (int idx = 0; idx < S; ++idx) {
+      const int sn = i * S + idx;
+      const u32x4 v = vnext;
+      if (sn + 1 < total) {
+        if (total - sn - 2 >= kRing - 2) wait_vmcnt<kRing - 2>();
+        else wait_vmcnt<0>();
+        vnext = read_slot(sn + 1);
+      }
+      const uint32_t gr[4] = {v.x, v.y, v.z, v.w};
+      const int mm = idx / GPL, g = idx % GPL;
+      granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
+      if constexpr (WDT != MOE_BF16) {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[mm][n] = fmaf(-F::OFF * F::UNIT, gs[n][g], acc[mm][n]);
+      }
+      // the slot has been consumed (its data fed the FMAs above): refill it
+#pragma unroll
+      for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(acc[mm][n]) : "v"(v.x), "v"(v.w) : "memory");
+      if (sn + kRing < total) issue(sn + kRing);
+    }
+    const int rl = wave + i * kWaves;
+    float red[NM][NT];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) red[m][n] = group_sum(acc[m][n], 64);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      if (n < nt && lane == n) {
+        float sa = 1.f, sb = 1.f;
+        if constexpr (WDT != MOE_BF16) {
+          sa = L.scale[0][rl] * (1.0f / F::UNIT);
+          if constexpr (PAIR) sb = L.scale[1][rl] * (1.0f / F::UNIT);
+        }
+        if constexpr (PAIR) {
+          const float gv = red[0][n] * sa, uv = red[1][n] * sb;
+          L.out[n][rl] = gv / (1.0f + expf(-gv)) * uv;
+        } else {
+          L.out[n][rl] = red[0][n] * sa;
+        }
+      }
+    }
+  }
+}
+
+// Which matrix and which token rows a block handles.  Routed and shared
+// blocks are interleaved evenly over the grid, so that the CUs each get a mix
+// of the two (their unpack costs per byte differ).
 struct BlockWork {
   bool shared;
   int e, p0, nrows, rb_index;
 };
 
 __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
-  const int bid = blockIdx.x;
-  const int routed_blocks = a.n_slots * a.nb;
-  if (bid < routed_blocks) {
-    const int slot = bid / a.nb;
+  const int64_t bid = blockIdx.x;
+  const int64_t routed_blocks = (int64_t)a.n_slots * a.nb;
+  const int64_t nblk = routed_blocks + a.nb_s;
+  const int64_t before = bid * a.nb_s / nblk;           // shared blocks before bid
+  const bool is_shared = (bid + 1) * a.nb_s / nblk > before;
+  if (!is_shared) {
+    const int rbid = (int)(bid - before);
+    const int slot = rbid / a.nb;
     bw.shared = false;
-    bw.rb_index = bid - slot * a.nb;
+    bw.rb_index = rbid - slot * a.nb;
     const RowSource& src = a.src;
     if (src.routed) {
       if (slot >= *src.n_active) return false;
@@ -367,7 +613,7 @@ __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
     }
   } else {
     bw.shared = true;
-    bw.rb_index = bid - routed_blocks;
+    bw.rb_index = (int)before;
     bw.e = 0;
     bw.p0 = 0;
     bw.nrows = a.n_tok;
@@ -399,12 +645,24 @@ __device__ __forceinline__ Job make_job(const GemvArgs& a, const BlockWork& bw, 
 }
 
 template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN>
-__device__ void run_block(const GemvArgs& a, const BlockWork& bw) {
+__device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
   const Job jb = make_job(a, bw, DOWN);
   if (jb.r0 >= jb.rows) return;
   const RowSource& src = a.src;
-  const void* in = DOWN ? (bw.shared ? a.h_s : a.h) : a.x;
+  const void* in = DOWN ? (bw.shared ? a.h_s : a.h) : (bw.shared && a.x_s ? a.x_s : a.x);
   void* out = DOWN ? (void*)(bw.shared ? a.y_s : a.y) : (bw.shared ? a.h_s : a.h);
+  // 16-byte granules on rows of >= 64 granules take the ring path (the
+  // launcher keeps blocks within kMaxRingRows rows); slices longer than one
+  // granule only occur on such rows, so the register path is compiled for
+  // one-granule slices and int2 only
+  constexpr bool kRingFmt = Fmt<WDT>::GB == 16;
+  constexpr bool kChunk = !kRingFmt || KSL == Fmt<WDT>::EPG;
+  constexpr int EPG = Fmt<WDT>::EPG, AB = ABF16 ? 2 : 4;
+  const bool ring = kRingFmt && jb.lpr == 64;
+  if (!ring && !kChunk) return;
+  const int nr = min(jb.nr, jb.rows - jb.r0);
+  static_assert(NTMAX == 1 || KSL <= 32, "two-token passes need short slices");
+  constexpr int NT2 = NTMAX >= 2 ? 2 : 1;
   for (int i0 = 0; i0 < bw.nrows; i0 += NTMAX) {
     const int nt = min(NTMAX, bw.nrows - i0);
     int64_t xo[NTMAX], dr[NTMAX];
@@ -423,10 +681,42 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw) {
         dr[n] = (int64_t)bw.p0 + i;
       }
     }
-    if (NTMAX >= 2 && KSL <= 64 && nt >= 2)
-      job_chunk<WDT, KSL, (NTMAX >= 2 && KSL <= 64 ? 2 : 1), ABF16, !DOWN>(jb, in, xo, nt, out, dr);
-    else
-      job_chunk<WDT, KSL, 1, ABF16, !DOWN>(jb, in, xo, 1, out, dr);
+    if constexpr (kRingFmt) {
+      if (ring) {
+        const bool first = i0 == 0;
+        if (a.in_sliced) {
+          if (NT2 == 2 && nt >= 2)
+            job_ring<WDT, KSL, NT2, ABF16, !DOWN, true>(jb, nr, in, xo, nt, first, L);
+          else
+            job_ring<WDT, KSL, 1, ABF16, !DOWN, true>(jb, nr, in, xo, 1, first, L);
+        } else {
+          if (NT2 == 2 && nt >= 2)
+            job_ring<WDT, KSL, NT2, ABF16, !DOWN, false>(jb, nr, in, xo, nt, first, L);
+          else
+            job_ring<WDT, KSL, 1, ABF16, !DOWN, false>(jb, nr, in, xo, 1, first, L);
+        }
+        __syncthreads();
+        const int ntw = (NT2 == 2 && nt >= 2) ? nt : 1;
+        const bool sl = !DOWN && a.out_sliced;
+        for (int t = threadIdx.x; t < ntw * nr; t += kThreads) {
+          const int n = t / nr, rl = t - n * nr;
+          const int64_t col = jb.r0 + rl;
+          const int64_t o = dr[n] * jb.rows + (sl ? sliced_index(col, EPG, AB) : col);
+          if (!DOWN && ABF16)
+            reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(L.out[n][rl]);
+          else
+            reinterpret_cast<float*>(out)[o] = L.out[n][rl];
+        }
+        __syncthreads();
+        continue;
+      }
+    }
+    if constexpr (kChunk) {
+      if (NT2 == 2 && nt >= 2)
+        job_chunk<WDT, KSL, NT2, ABF16, !DOWN>(jb, in, xo, nt, out, dr);
+      else
+        job_chunk<WDT, KSL, 1, ABF16, !DOWN>(jb, in, xo, 1, out, dr);
+    }
   }
 }
 
@@ -435,13 +725,14 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw) {
 // n_active exit at once) and, optionally, the shared expert (nb_s blocks).
 
 template <int WR, int KR, int WS, int KS, int NTMAX, int ABF16, bool DOWN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KR > 64 || KS > 64 ? 2 : 3, 8))) void k_gemv(GemvArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_gemv(GemvArgs a) {
+  __shared__ RingLds lds;
   BlockWork bw;
   if (!block_work(a, bw)) return;
   if (bw.shared)
-    run_block<WS, KS, NTMAX, ABF16, DOWN>(a, bw);
+    run_block<WS, KS, NTMAX, ABF16, DOWN>(a, bw, lds);
   else
-    run_block<WR, KR, NTMAX, ABF16, DOWN>(a, bw);
+    run_block<WR, KR, NTMAX, ABF16, DOWN>(a, bw, lds);
 }
 
 
@@ -449,7 +740,7 @@ template <int WR, int KR, int WS, int KS, bool DOWN>
 hipError_t gemv_go(const GemvArgs& a, int ntmax, int act_bf16, unsigned blocks, hipStream_t s) {
 #define MOE_K(NT, AB) \
   hipLaunchKernelGGL((k_gemv<WR, KR, WS, KS, NT, AB, DOWN>), dim3(blocks), dim3(kThreads), 0, s, a)
-  if constexpr (KR <= 64) {
+  if constexpr (KR <= 32) {
     if (ntmax >= 2) {
       if (act_bf16) MOE_K(2, 1); else MOE_K(2, 0);
       return hipGetLastError();

@@ -38,6 +38,11 @@ bool gemv_supported(int dtype, int32_t K) {
   return make_geo(dtype, K, g);
 }
 
+bool gemv_ring(int dtype, int32_t K) {
+  MatGeo g;
+  return (dtype == MOE_I4 || dtype == MOE_BF16) && make_geo(dtype, K, g) && g.lpr == 64;
+}
+
 bool gemv_pair_supported(int dtype, int32_t K, int sdtype, int32_t Ks) {
   MatGeo g, gs;
   if (!make_geo(dtype, K, g) || !make_geo(sdtype, Ks, gs)) return false;
@@ -58,12 +63,15 @@ static int rows_per_block(const MatGeo& g, int dtype, int K, int rows, bool pair
   int64_t passes = bytes_per_wave / (row_bytes_of(dtype, K, pair) * g.rpp);
   if (passes < 1) passes = 1;
   int64_t rb = passes * kWaves * g.rpp;
+  if (rb > kMaxRingRows) rb = kMaxRingRows / (kWaves * g.rpp) * (kWaves * g.rpp);
   if (rb > rows) rb = rows;
   return (int)(rb < 1 ? 1 : rb);
 }
 
-// Waves a launch aims for: 256 CUs x 8 resident waves, one round.
+// Waves a launch aims for: 256 CUs x 8 resident waves (two 4-wave blocks per
+// CU: the ring path's LDS and the register budget allow two), one round.
 constexpr int64_t kTargetWaves = 2048;
+constexpr int64_t kTargetBlocks = kTargetWaves / kWaves;
 constexpr int64_t kMinBytesPerWave = 8 * 1024;
 
 hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
@@ -79,15 +87,25 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     shared_dtype = dtype;
   }
   // bytes the launch streams (routed slots bounded by n_slots), split evenly
+  // over the waves of one resident round; blocks whose rows are rounded up
+  // must not spill into a second round, so grow the share until they fit
   const int64_t mat = row_bytes_of(dtype, kin, !down) * rows;
   const int64_t mat_s = a.has_shared ? row_bytes_of(shared_dtype, kin_s, !down) * rows_s : 0;
   int64_t per_wave = ((int64_t)a.n_slots * mat + mat_s) / kTargetWaves;
   if (per_wave < kMinBytesPerWave) per_wave = kMinBytesPerWave;
-  a.rb = rows_per_block(a.geo, dtype, kin, rows, !down, per_wave);
-  a.nb = (rows + a.rb - 1) / a.rb;
-  a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave) : 1;
-  const int nb_s = a.has_shared ? (rows_s + a.rb_s - 1) / a.rb_s : 0;
-  const long long blocks = (long long)a.n_slots * a.nb + nb_s;
+  int nb_s = 0;
+  long long blocks = 0;
+  // (nb_s is kept in a.nb_s for the kernel's block mapping)
+  for (int it = 0; it < 64; ++it) {
+    a.rb = rows_per_block(a.geo, dtype, kin, rows, !down, per_wave);
+    a.nb = (rows + a.rb - 1) / a.rb;
+    a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave) : 1;
+    nb_s = a.has_shared ? (rows_s + a.rb_s - 1) / a.rb_s : 0;
+    blocks = (long long)a.n_slots * a.nb + nb_s;
+    if (blocks <= kTargetBlocks) break;
+    per_wave += per_wave / 16 + 1;
+  }
+  a.nb_s = nb_s;
   if (blocks <= 0 || max_rows_per_slot <= 0) return hipSuccess;
   const int ntmax = max_rows_per_slot >= 2 ? 2 : 1;
   const unsigned nblk = (unsigned)blocks;

@@ -95,4 +95,32 @@ hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int
   return hipGetLastError();
 }
 
+// Sliced copies of activation rows (layout in moe_internal.h): every thread
+// moves one 16-byte piece per format; the writes are coalesced, the reads
+// gather the piece's P consecutive activations.
+__global__ __launch_bounds__(256) void k_slice_rows(const uint8_t* __restrict__ x, int32_t ab,
+                                                    int32_t K, int32_t T, int32_t epg_a,
+                                                    uint8_t* __restrict__ dst_a, int32_t epg_b,
+                                                    uint8_t* __restrict__ dst_b) {
+  const int64_t pieces = (int64_t)K * ab / 16;
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = blockIdx.y;
+  if (p >= pieces || t >= T) return;
+  const int64_t row = t * K * ab;
+  if (dst_a && epg_a > 0) slice_piece(x + row, dst_a + row, p, epg_a, ab);
+  if (dst_b && epg_b > 0) slice_piece(x + row, dst_b + row, p, epg_b, ab);
+}
+
+hipError_t launch_slice_rows(const void* x, int act_bf16, int32_t T, int32_t K, int32_t epg_a,
+                             void* dst_a, int32_t epg_b, void* dst_b, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int ab = act_bf16 ? 2 : 4;
+  const int64_t pieces = (int64_t)K * ab / 16;
+  const dim3 grid((unsigned)((pieces + 255) / 256), (unsigned)T);
+  hipLaunchKernelGGL(k_slice_rows, grid, dim3(256), 0, s, reinterpret_cast<const uint8_t*>(x), ab,
+                     K, T, epg_a, reinterpret_cast<uint8_t*>(dst_a), epg_b,
+                     reinterpret_cast<uint8_t*>(dst_b));
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -60,9 +60,23 @@ constexpr int LG_QT = 8;
 __global__ __launch_bounds__(256) void k_logits_gemv(const float* __restrict__ W,
                                                      const void* __restrict__ x, int act_bf16,
                                                      int32_t T, int32_t H, int32_t E,
-                                                     double* __restrict__ z) {
+                                                     double* __restrict__ z, SliceReq sr) {
   __shared__ double red[kDecodeTokens][256];
   const int e = blockIdx.x, tid = threadIdx.x;
+  // the blocks also share out the sliced copies of the rows
+  {
+    const int ab = act_bf16 ? 2 : 4;
+    const int64_t pieces = (int64_t)H * ab / 16;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    for (int64_t p = (int64_t)e * 256 + tid; p < pieces; p += (int64_t)E * 256)
+      for (int n = 0; n < T; ++n) {
+        const int64_t row = (int64_t)n * H * ab;
+        if (sr.dst_a && sr.epg_a > 0)
+          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_a) + row, p, sr.epg_a, ab);
+        if (sr.dst_b && sr.epg_b > 0)
+          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_b) + row, p, sr.epg_b, ab);
+      }
+  }
   const float* wr = W + (int64_t)e * H;
   const int nq = H / 4;
   const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -168,12 +182,18 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
 }
 
 hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
-                                int32_t H, int32_t E, double* z, hipStream_t s) {
+                                int32_t H, int32_t E, double* z, const SliceReq& sr,
+                                hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (T <= kDecodeTokens) {
     hipLaunchKernelGGL(k_logits_gemv, dim3(E), dim3(256), 0, s, w_router, x, act_bf16, T, H, E,
-                       z);
+                       z, sr);
   } else {
+    if (sr.dst_a || sr.dst_b) {
+      const hipError_t st = launch_slice_rows(x, act_bf16, T, H, sr.epg_a, sr.dst_a, sr.epg_b,
+                                              sr.dst_b, s);
+      if (st != hipSuccess) return st;
+    }
     dim3 grid((T + LG_BT - 1) / LG_BT, (E + LG_BE - 1) / LG_BE);
     hipLaunchKernelGGL(k_logits_gemm, grid, dim3(256), 0, s, w_router, x, act_bf16, T, H, E, z);
   }

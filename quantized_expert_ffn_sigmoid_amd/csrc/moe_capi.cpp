@@ -78,10 +78,14 @@ ExpertSetDev dev_set(const moe_expert_set& s) {
   return v;
 }
 
+// Elements per 16-byte granule of a weight format (the unit of the sliced
+// activation layout).
+int32_t epg_of(int32_t dtype) { return dtype == MOE_BF16 ? 8 : 32; }
+
 // Workspace carve for n tokens.  Every region is 256-byte aligned.
 struct Carve {
   size_t z, idx, w, counts, offsets, entries, inverse, active, n_active, h, h_sh, Y, S, xn, yl,
-      total;
+      xs, xs_sh, total;
 };
 
 Carve carve(const moe_layer_desc& d, int64_t T) {
@@ -109,6 +113,8 @@ Carve carve(const moe_layer_desc& d, int64_t T) {
   c.S = take(sizeof(float) * T * H);
   c.xn = take(sizeof(float) * T * H);
   c.yl = take(sizeof(float) * T * H);
+  c.xs = take(sizeof(float) * T * H);
+  c.xs_sh = take(sizeof(float) * T * H);
   c.total = o;
   return c;
 }
@@ -158,8 +164,28 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   float* Y = at<float>(ws, c.Y);
   float* S = at<float>(ws, c.S);
 
+  // Sliced activation rows (a coalesced per-lane layout) for the expert
+  // kernels that stream their weights through the LDS ring.
+  const bool has_sh = d.n_shared > 0;
+  const int32_t Ish = I * (has_sh ? d.n_shared : 1);
+  const bool gu_ring = gemv_ring(d.expert_dtype, H) && (!has_sh || gemv_ring(d.shared_dtype, H));
+  const bool dn_ring = gemv_ring(d.expert_dtype, I) && (!has_sh || gemv_ring(d.shared_dtype, Ish));
+  const int epg_r = epg_of(d.expert_dtype), epg_s = has_sh ? epg_of(d.shared_dtype) : 0;
+  void* xs = at<void>(ws, c.xs);
+  void* xs_sh = epg_s && epg_s != epg_r ? at<void>(ws, c.xs_sh) : xs;
+
+  SliceReq sr{};
+  if (gu_ring) {
+    sr.epg_a = epg_r;
+    sr.dst_a = xs;
+    if (xs_sh != xs) {
+      sr.epg_b = epg_s;
+      sr.dst_b = xs_sh;
+    }
+  }
+
   record(opts, MOE_STAGE_ROUTE, 0, s);
-  MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, s));
+  MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, sr, s));
   const bool fused_route = T <= kDecodeTokens;
   if (fused_route)
     MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
@@ -186,19 +212,23 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   g.n_tok = T;
   g.H = H;
   g.I = I;
-  g.Is = I * (d.n_shared > 0 ? d.n_shared : 1);
+  g.Is = Ish;
   g.n_slots = (int64_t)T * K < E ? T * K : E;
-  g.x = x;
+  g.x = gu_ring ? xs : x;
+  g.x_s = gu_ring ? xs_sh : nullptr;
   g.h = h;
   g.h_s = h_sh;
   g.y = Y;
   g.y_s = S;
+  g.in_sliced = gu_ring;
+  g.out_sliced = gu_ring && dn_ring;
 
   record(opts, MOE_STAGE_GATE_UP, 0, s);
   MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_GATE_UP, 1, s);
 
   record(opts, MOE_STAGE_DOWN, 0, s);
+  g.in_sliced = g.out_sliced;
   MOE_TRY(launch_gemv(g, true, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_DOWN, 1, s);
 
@@ -245,7 +275,7 @@ moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* z = at<double>(ws, carve(*d, n_tokens).z);
   if (launch_router_logits(w_router, x, d->act_dtype == MOE_BF16, n_tokens, d->hidden,
-                           d->n_experts, z, s) != hipSuccess)
+                           d->n_experts, z, SliceReq{}, s) != hipSuccess)
     return MOE_EHIP;
   if (launch_router_select(*d, z, bias, n_tokens, topk_idx, topk_w, s) != hipSuccess)
     return MOE_EHIP;
@@ -301,9 +331,12 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, in
   g.x = x;
   g.h = at<void>(ws, carve(*d, n_rows).h);
   g.y = y;
+  g.in_sliced = 0;
+  g.out_sliced = gemv_ring(dtype, d->hidden) && gemv_ring(dtype, I);
   if (launch_gemv(g, false, dtype, dtype, act_bf16, n_rows, s) != hipSuccess) return MOE_EHIP;
   g.src.rows = nullptr;   // down reads h rows 0..n_rows-1 and writes y rows 0..n_rows-1
   g.src.row_div = 1;
+  g.in_sliced = g.out_sliced;
   if (launch_gemv(g, true, dtype, dtype, act_bf16, n_rows, s) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }

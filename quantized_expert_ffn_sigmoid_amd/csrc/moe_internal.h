@@ -80,13 +80,22 @@ struct GemvArgs {
   int32_t H, I, Is;        // Is: shared intermediate size
   int32_t n_slots;         // routed slots in the grid
   const void* x;           // gate/up input rows [*][H] (act dtype)
+  const void* x_s;         // gate/up input rows of the shared expert (null: x)
   void* h;                 // routed h rows [bucket position][I] (act dtype)
   void* h_s;               // shared h rows [token][Is]
+  // Row layouts.  A "sliced" row of K activations, for a weight format of EPG
+  // elements per 16-byte granule, stores the P = 16 / act_bytes activations of
+  // piece c of granule q = g * 64 + j at ((g * (EPG / P) + c) * 64 + j) * P, so
+  // that lane j of a wave reads its granules' activations with coalesced
+  // loads.  in_sliced: this launch's input rows (x / x_s, or h / h_s) are
+  // sliced for the matrix that consumes them; out_sliced: gate/up writes h and
+  // h_s sliced for the down matrices of the same sets.
+  int32_t in_sliced, out_sliced;
   float* y;                // routed down output rows [slot f][H]
   float* y_s;              // shared down output rows [token][H]
   // filled in by the launcher
   MatGeo geo, geo_s;
-  int32_t rb, nb, rb_s;
+  int32_t rb, nb, rb_s, nb_s;
 };
 
 // ------------------------------------------------------------- launchers
@@ -95,8 +104,22 @@ struct GemvArgs {
 
 hipError_t launch_rmsnorm(const float* x, float* out, int32_t T, int32_t H, float eps,
                           hipStream_t s);
+// Sliced copies of activation rows for up to two weight formats (epg 0 or
+// dst null: skipped); see GemvArgs for the layout.
+struct SliceReq {
+  int32_t epg_a, epg_b;
+  void* dst_a;
+  void* dst_b;
+};
+// Router logits; for T <= kDecodeTokens the same launch also writes the
+// sliced copies that sr asks for (larger T: launch_slice_rows).
 hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
-                                int32_t H, int32_t E, double* z, hipStream_t s);
+                                int32_t H, int32_t E, double* z, const SliceReq& sr,
+                                hipStream_t s);
+// Copies of the T activation rows in the sliced layouts of up to two weight
+// formats (epg 0 or dst null: skipped).
+hipError_t launch_slice_rows(const void* x, int act_bf16, int32_t T, int32_t K, int32_t epg_a,
+                             void* dst_a, int32_t epg_b, void* dst_b, hipStream_t s);
 hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const float* bias,
                                 int32_t T, int32_t* topk_idx, float* topk_w, hipStream_t s);
 hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_idx,
@@ -130,5 +153,29 @@ bool gemv_supported(int dtype, int32_t K);
 // Whether a routed set (dtype, input K) and the shared set (sdtype, input Ks)
 // can share one launch: both covered, with the same per-lane slice geometry.
 bool gemv_pair_supported(int dtype, int32_t K, int sdtype, int32_t Ks);
+// Whether the expert GEMV of this format streams rows of length K through the
+// LDS ring (rows of >= 64 granules of 16 bytes), the path that reads sliced
+// activation rows.
+bool gemv_ring(int dtype, int32_t K);
+
+// Moves 16-byte piece p of the sliced copy (epg) of a row of K activations of
+// ab bytes from the row-major row.
+__device__ __forceinline__ void slice_piece(const uint8_t* row, uint8_t* dst_row, int64_t p,
+                                            int epg, int ab) {
+  const int P = 16 / ab, ppc = epg / P;
+  const int64_t j = p & 63, gc = p >> 6;
+  const int64_t g = gc / ppc, c = gc - g * ppc;
+  const int64_t e0 = (g * 64 + j) * epg + c * P;
+  *reinterpret_cast<uint4*>(dst_row + p * 16) = *reinterpret_cast<const uint4*>(row + e0 * ab);
+}
+
+// Element index of activation e of a row in the sliced layout (see GemvArgs).
+__host__ __device__ __forceinline__ int64_t sliced_index(int64_t e, int epg, int act_bytes) {
+  const int P = 16 / act_bytes;
+  const int64_t q = e / epg;
+  const int64_t g = q >> 6, j = q & 63;
+  const int64_t c = (e % epg) / P, u = e % P;
+  return ((g * (epg / P) + c) * 64 + j) * P + u;
+}
 
 }  // namespace moe
