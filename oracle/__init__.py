@@ -95,6 +95,7 @@ def lib():
             "orc_expert_ffn": [D, S, i32, i32, vp, vp, i32, i32, vp],
             "orc_layer_forward": [D, vp, vp, S, S, vp, i32, vp, vp, vp],
             "orc_layer_forward_per_token": [D, vp, vp, S, S, vp, i32, vp],
+            "orc_layer_band": [D, vp, vp, S, S, vp, i32, dbl, vp],
             "orc_rmsnorm": [vp, i32, i32, dbl, vp],
             "orc_residual_add": [vp, vp, i64],
             "orc_set_threads": [i32],
@@ -244,6 +245,19 @@ def layer_forward_per_token(d: Desc, w_router, bias, routed: ExpertSet,
     return out
 
 
+def layer_band(d: Desc, w_router, bias, routed: ExpertSet, shared: Optional[ExpertSet], x,
+               n_tokens, rel_window: float) -> np.ndarray:
+    """Output band of the bf16 rounding of h (see moe_oracle.h); zeros for f32
+    activations."""
+    band = np.empty((n_tokens, d.hidden), dtype=np.float64)
+    if n_tokens:
+        _check(lib().orc_layer_band(ctypes.byref(d.c()), _p(w_router), _p(bias),
+                                    ctypes.byref(routed.c),
+                                    ctypes.byref(shared.c) if shared else None, _p(x),
+                                    n_tokens, float(rel_window), _p(band)))
+    return band
+
+
 def rmsnorm(x: np.ndarray, eps: float) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty_like(x)
@@ -283,6 +297,16 @@ def layer_forward_host(hl, x: np.ndarray, desc: Optional[Desc] = None):
     idx, _, _ = route(d, hl.w_router, hl.bias, x, T)
     routed = expert_set_from_host_layer(hl, np.unique(idx))
     return layer_forward(d, hl.w_router, hl.bias, routed, shared_set_from_host_layer(hl), x, T)
+
+
+def layer_band_host(hl, x: np.ndarray, rel_window: float, desc: Optional[Desc] = None):
+    """layer_band for a gen.HostLayer, generating only the selected experts."""
+    d = desc or Desc.from_config(hl.cfg, expert_dtype=hl.dtype)
+    T = x.shape[0]
+    idx, _, _ = route(d, hl.w_router, hl.bias, x, T)
+    routed = expert_set_from_host_layer(hl, np.unique(idx))
+    return layer_band(d, hl.w_router, hl.bias, routed, shared_set_from_host_layer(hl), x, T,
+                      rel_window)
 
 
 def stack_forward_host(layers, x: np.ndarray, eps: float):

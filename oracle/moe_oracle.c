@@ -38,6 +38,10 @@
  *                        reductions to plain top-k, closed-form weights.
  *   orc_route            = orc_logits + orc_select.
  *   orc_bucket           numpy stable argsort; permutation invariants.
+ *   orc_layer_band       a test tolerance, not part of the layer: zero for f32
+ *                        activations and for a zero window, monotone in the
+ *                        window, and equal to the sum over every h at the
+ *                        widest window (checked against orc_dequant_rows).
  *   orc_expert_ffn       worked H=2,I=1 example; integer-matrix case against
  *                        numpy matmul and scipy's logistic; scale factoring.
  *   orc_layer_forward    dense evaluation of all experts; batch-union equals
@@ -381,6 +385,92 @@ int orc_expert_ffn(const orc_desc* d, const orc_expert_set* set, int32_t expert,
   }
   free(xv);
   free(hb);
+  return rc;
+}
+
+/* ------------------------------------------------------- bf16 twin band -- */
+
+/* Rounding h to bf16 (act bf16) is a decision that floating point takes: a
+ * kernel that accumulates in fp32 in another order lands a value lying very
+ * near a rounding midpoint on either side of it, and both roundings are
+ * correct results of the layer as defined ("muse-glimmer-intel-serve"
+ * introduction: the low-precision twin defines the deviation band).  For
+ * every h whose float value lies within rel_window * |h| of the midpoint
+ * between its two bf16 neighbours, the other neighbour is also valid; the
+ * band of an output is the largest change such alternatives can make to it:
+ *   band[t][o] = sum_j |w_tj| * sum_{r ambiguous} |down_o,r| * |h_alt - h_bf16|
+ * plus the same sum over the shared expert (weight 1).  Zero when
+ * activations are f32. */
+static void ffn_band_one(int32_t dtype, const void* gu, const float* gus, const void* dn,
+                         const float* dns, int64_t H, int64_t I, const double* xv,
+                         double rel_window, double weight, double* dh, double* band) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < I; ++r) {
+    double g = 0.0, u = 0.0;
+    for (int64_t c = 0; c < H; ++c) g += weight_at(dtype, gu, gus, H, r, c) * xv[c];
+    for (int64_t c = 0; c < H; ++c) u += weight_at(dtype, gu, gus, H, I + r, c) * xv[c];
+    const float hf = (float)(g / (1.0 + exp(-g)) * u);
+    uint32_t bits;
+    memcpy(&bits, &hf, 4);
+    dh[r] = 0.0;
+    if ((bits & 0x7F800000u) == 0x7F800000u) continue;
+    const uint32_t lo_bits = bits & 0xFFFF0000u, hi_bits = lo_bits + 0x10000u;
+    float lo, hi;
+    memcpy(&lo, &lo_bits, 4);
+    memcpy(&hi, &hi_bits, 4);
+    const double mid = 0.5 * ((double)lo + (double)hi);
+    if (fabs((double)hf - mid) <= rel_window * fabs((double)hf)) dh[r] = fabs((double)hi - (double)lo);
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t o = 0; o < H; ++o) {
+    double acc = 0.0;
+    for (int64_t r = 0; r < I; ++r)
+      if (dh[r] != 0.0) acc += fabs(weight_at(dtype, dn, dns, I, o, r)) * dh[r];
+    band[o] += weight * acc;
+  }
+}
+
+int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
+                   const orc_expert_set* routed, const orc_expert_set* shared, const void* x,
+                   int32_t n_tokens, double rel_window, double* band) {
+  if (!desc_ok(d) || rel_window < 0.0) return ORC_EINVAL;
+  const int64_t H = d->hidden, K = d->top_k;
+  for (int64_t i = 0; i < (int64_t)n_tokens * H; ++i) band[i] = 0.0;
+  if (n_tokens == 0 || !d->act_bf16) return ORC_OK;
+  const int64_t Is = (int64_t)d->inter * (d->n_shared > 1 ? d->n_shared : 1);
+  int32_t* idx = (int32_t*)malloc(sizeof(int32_t) * (size_t)n_tokens * (size_t)K);
+  double* w64 = (double*)malloc(sizeof(double) * (size_t)n_tokens * (size_t)K);
+  double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+  double* dh = (double*)malloc(sizeof(double) * (size_t)Is);
+  int rc = orc_route(d, w_router, bias, x, n_tokens, idx, NULL, w64);
+  for (int64_t t = 0; t < n_tokens && rc == ORC_OK; ++t) {
+    for (int64_t c = 0; c < H; ++c) xv[c] = x_at(x, 1, t * H + c);
+    for (int64_t j = 0; j < K && rc == ORC_OK; ++j) {
+      const int32_t e = idx[t * K + j];
+      if (!set_has(routed, e)) {
+        rc = ORC_EMISSING;
+        break;
+      }
+      ffn_band_one(routed->dtype, routed->gate_up[e],
+                   routed->gate_up_scale ? routed->gate_up_scale[e] : 0, routed->down[e],
+                   routed->down_scale ? routed->down_scale[e] : 0, H, d->inter, xv, rel_window,
+                   fabs(w64[t * K + j]), dh, band + t * H);
+    }
+    if (rc == ORC_OK && d->n_shared > 0) {
+      if (!set_has(shared, 0)) {
+        rc = ORC_EMISSING;
+        break;
+      }
+      ffn_band_one(shared->dtype, shared->gate_up[0],
+                   shared->gate_up_scale ? shared->gate_up_scale[0] : 0, shared->down[0],
+                   shared->down_scale ? shared->down_scale[0] : 0, H, Is, xv, rel_window, 1.0,
+                   dh, band + t * H);
+    }
+  }
+  free(idx);
+  free(w64);
+  free(xv);
+  free(dh);
   return rc;
 }
 

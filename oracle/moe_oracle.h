@@ -63,6 +63,13 @@ int orc_layer_forward(const orc_desc* d, const float* w_router, const float* bia
 int orc_layer_forward_per_token(const orc_desc* d, const float* w_router, const float* bias,
                                 const orc_expert_set* routed, const orc_expert_set* shared,
                                 const void* x, int32_t n_tokens, double* out);
+/* Output band of the bf16 rounding of h (act bf16 only; zero otherwise):
+ * band[t][o] bounds the change of out[t][o] when every h whose float value
+ * lies within rel_window * |h| of a bf16 rounding midpoint takes the other
+ * rounding.  A test tolerance, not part of the layer. */
+int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
+                   const orc_expert_set* routed, const orc_expert_set* shared, const void* x,
+                   int32_t n_tokens, double rel_window, double* band);
 int orc_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, double eps, float* out);
 int orc_residual_add(float* x, const double* y, int64_t n);
 void orc_set_threads(int32_t n);
