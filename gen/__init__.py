@@ -68,15 +68,26 @@ class Config:
     zipf_lambda: float = 0.0
 
 
-ZIPF_LAMBDA_FILE = os.path.join(HERE, "zipf_lambda.json")
+# Router bias of the Zipf-skewed workload, by popularity rank: calibrated once
+# on the prefill batch by oracle/calibrate_zipf_bias.py (see there) and stored
+# as data; expert e of a layer takes the entry of its rank in that layer's
+# seeded rank permutation.
+ZIPF_BIAS_FILE = os.path.join(HERE, "zipf_bias.json")
+_zipf_bias_cache = {}
 
 
-def _zipf_lambda() -> float:
+def zipf_bias_by_rank(n_experts: int, top_k: int, s: float) -> Optional[np.ndarray]:
     import json
-    if os.path.exists(ZIPF_LAMBDA_FILE):
-        with open(ZIPF_LAMBDA_FILE) as f:
-            return float(json.load(f)["lambda"])
-    return 0.25
+    key = (n_experts, top_k, s)
+    if key not in _zipf_bias_cache:
+        val = None
+        if os.path.exists(ZIPF_BIAS_FILE):
+            with open(ZIPF_BIAS_FILE) as f:
+                doc = json.load(f)
+            if (doc["n_experts"], doc["top_k"], doc["s"]) == key:
+                val = np.asarray(doc["bias_by_rank"], dtype=np.float32)
+        _zipf_bias_cache[key] = val
+    return _zipf_bias_cache[key]
 
 
 _GLM = dict(hidden=6144, inter=2048, n_experts=256, top_k=8, router=SIGMOID_NOAUX_TC,
@@ -103,8 +114,6 @@ CONFIGS = {
 
 def get_config(name: str, **overrides) -> Config:
     cfg = CONFIGS[name]
-    if cfg.bias == "zipf" and "zipf_lambda" not in overrides:
-        overrides["zipf_lambda"] = _zipf_lambda()
     return replace(cfg, **overrides) if overrides else cfg
 
 
@@ -265,10 +274,15 @@ def router(cfg: Config, layer: int = 0):
     if cfg.bias == "normal":
         return w, normal_f32((cfg.n_experts,), cfg.seed, layer, T_BIAS, 0, cfg.bias_std)
     if cfg.bias == "zipf":
-        p = zipf_targets(cfg.n_experts, cfg.top_k, cfg.zipf_s)
         rank = zipf_ranks(cfg, layer)
-        b = (cfg.zipf_lambda * np.log(p[rank - 1])).astype(np.float32)
-        return w, b
+        table = zipf_bias_by_rank(cfg.n_experts, cfg.top_k, cfg.zipf_s)
+        if table is None or cfg.zipf_lambda:
+            # no calibration for this shape: a log-popularity bias of strength
+            # zipf_lambda (0.25 unless set) keeps the skew qualitatively
+            lam = cfg.zipf_lambda or 0.25
+            p = zipf_targets(cfg.n_experts, cfg.top_k, cfg.zipf_s)
+            return w, (lam * np.log(p[rank - 1])).astype(np.float32)
+        return w, table[rank - 1].copy()
     raise ValueError(cfg.bias)
 
 
