@@ -138,7 +138,8 @@ moe_status moe_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const 
  * `expert` of `set` (dtype expert_dtype, intermediate I); shared = 1 the shared
  * expert (shared_dtype, intermediate n_shared*I; `expert` must be 0).
  * x: [*][H] act_dtype; y: [n_rows][H] fp32.  Workspace: moe_workspace_bytes(d,
- * n_rows). */
+ * n_rows).  Runs on the GEMV kernels: MOE_EUNSUPPORTED when they do not cover
+ * the expert's shapes. */
 moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, int32_t shared,
                           int32_t expert, const void* x, const int32_t* rows, int32_t n_rows,
                           int32_t row_div, float* y, void* ws, size_t ws_bytes, void* stream);
@@ -147,7 +148,13 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, in
  * of its tokens, and combine: out[t] = sum_j topk_w[t][j] * FFN_{e_tj}(x_t)
  * (j ascending) + shared(x_t).  x: [n_tokens][H] act_dtype; out: [n_tokens][H]
  * fp32.  topk_idx_out / topk_w_out ([n_tokens][k]) are optional copies of the
- * routing.  Workspace: moe_workspace_bytes(d, n_tokens). */
+ * routing.  Workspace: moe_workspace_bytes(d, n_tokens).
+ * Two expert paths: up to 16 tokens, dequant-on-use GEMV kernels; more
+ * tokens with act_dtype MOE_BF16, int4 or bf16 experts, H a multiple of 256
+ * and I (and n_shared*I) multiples of 128, a grouped GEMM on the matrix cores
+ * over 64-row bucket tiles (else the GEMV kernels).  A descriptor is valid
+ * when one path covers it; a call whose batch size selects a path that does
+ * not returns MOE_EUNSUPPORTED. */
 moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w, const void* x,
                              int32_t n_tokens, float* out, int32_t* topk_idx_out,
                              float* topk_w_out, void* ws, size_t ws_bytes, void* stream);

@@ -1,0 +1,555 @@
+// k_ggemm.hip -- batch-union grouped GEMM on the matrix cores (gfx950), for
+// buckets of prefill size.
+//
+// Each active expert applies its SwiGLU FFN to the rows of its bucket ("colibri"
+// README, "What's implemented": batch-union grouping, each unique expert read
+// once and applied to every position routed to it; "iliria" README: gate and
+// up over one activation, SwiGLU).  With thousands of tokens the buckets hold
+// tens to thousands of rows, so the expert contraction is a dense bf16
+// matrix product -- the one dense contraction of the layer -- and runs on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//
+// Tiles.  A block computes a 64-row tile of one bucket (or of the shared
+// expert's token rows) against 256 weight rows: for gate/up, 128 gate rows and
+// the 128 up rows paired with them, so SwiGLU is applied in registers; for down,
+// 256 output rows.  Each of the 4 waves owns 64 weight rows (four 16-row
+// N-subtiles) and all 64 tile rows (four 16-row M-subtiles): 16 accumulator
+// tiles.  The K dimension advances 128 at a time.
+//
+// Operands.  Activations (bf16) are staged per K step in LDS, double buffered,
+// rows padded to 272 bytes so that the 16-byte operand reads of 16 lanes fall
+// on distinct banks.  Weights go straight from HBM to registers: lane l reads
+// 16 bytes of weight row (l % 16) for its K group (l / 16), which are exactly
+// the operand elements it supplies.  int4 codes become exact bf16 values with
+// a shift and an AND-OR per pair of codes: the offset-binary code q + 8 in the
+// top mantissa bits of 1.0 is (24 + q) / 16.  The offset is removed in the
+// epilogue with the row sums of the activations (k_rowsum_bf16, one pass over
+// x and one over h).  The
+// pairing of nibbles (j, j + 4) in each converted register is matched by
+// storing each group of 8 activations in LDS in the order 0,4,1,5,2,6,3,7.
+// bf16 weights need neither step.  Per-row scales commute with the K sum and
+// are applied in the epilogue, as in the decode kernels.
+#include "moe_internal.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4g __attribute__((ext_vector_type(4)));
+
+constexpr int GG_BM = 64;          // tile rows (tokens / bucket positions)
+constexpr int GG_BK = 128;         // K per step
+constexpr int GG_WAVES = 4;
+constexpr int GG_THREADS = GG_WAVES * 64;
+constexpr int GG_NW = 64;          // weight rows per wave
+constexpr float GG_OFF = 24.0f;    // int4 operand = (GG_OFF + q) / GG_DIV
+constexpr float GG_DIV = 16.0f;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4g v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 int4 codes (one dword, low nibble first) -> 4 registers of bf16 pairs
+// (code j, code j + 4).  The offset-binary code u = q + 8 goes to the top four
+// mantissa bits of 1.0, giving 1 + u / 16 = (24 + q) / 16 exactly; of the
+// exact encodings with an implicit leading one this has the smallest offset
+// relative to the code, which keeps the fp32 accumulation error small.
+__device__ __forceinline__ u32x4g i4_to_bf16(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  u32x4g r;
+  r.x = ((u << 3) & 0x00780078u) | 0x3F803F80u;
+  r.y = ((u >> 1) & 0x00780078u) | 0x3F803F80u;
+  r.z = ((u >> 5) & 0x00780078u) | 0x3F803F80u;
+  r.w = ((u >> 9) & 0x00780078u) | 0x3F803F80u;
+  return r;
+}
+
+// Reorder 8 bf16 activations (x0..x7 in 4 dwords) to x0,x4,x1,x5,x2,x6,x3,x7.
+__device__ __forceinline__ u32x4g perm_0415(u32x4g d) {
+  u32x4g r;
+  r.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
+  r.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
+  r.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+  return r;
+}
+
+struct GgTile {
+  bool shared;
+  int e;          // expert (routed)
+  int p0;         // first bucket position (routed) or first token (shared)
+  int n;          // valid rows
+  int nt;         // n-tile index
+};
+
+__device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
+  const int64_t total = (int64_t)a.max_tiles * a.nt_r + (int64_t)a.s_tiles * a.nt_s;
+  const int64_t per = (total + 7) / 8;
+  // Consecutive logical tiles run on one XCD (blocks are dealt to the 8 XCDs
+  // round robin) at about the same time.  Logical order: expert, n-tile,
+  // m-tile -- the m-tiles of one expert that use the same weight rows run
+  // together and share them through L2, while the activation tiles they
+  // re-read for every n-tile are small enough to stay in the last-level
+  // cache.
+  const int64_t L = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (L >= total) return false;
+  const int64_t routed = (int64_t)a.max_tiles * a.nt_r;
+  if (L < routed) {
+    // the expert's m-tiles [first, first + cnt) occupy logical tiles
+    // [first * nt_r, (first + cnt) * nt_r), so L / nt_r is one of them
+    const int q0 = (int)(L / a.nt_r);
+    if (q0 >= *a.n_tiles) return false;
+    const int first = a.tile_first[q0], cnt = a.tile_cnt[q0];
+    const int64_t rem = L - (int64_t)first * a.nt_r;
+    t.nt = (int)(rem / cnt);
+    const int mt = first + (int)(rem - (int64_t)t.nt * cnt);
+    t.shared = false;
+    t.e = a.tile_e[mt];
+    t.p0 = a.tile_p0[mt];
+    t.n = a.tile_n[mt];
+  } else {
+    const int64_t L2 = L - routed;
+    t.nt = (int)(L2 / a.s_tiles);
+    const int mt = (int)(L2 - (int64_t)t.nt * a.s_tiles);
+    t.shared = true;
+    t.e = 0;
+    t.p0 = mt * GG_BM;
+    t.n = min(GG_BM, a.T - t.p0);
+  }
+  return t.n > 0;
+}
+
+// Activation stages in LDS: 64 rows x 256 bytes (128 bf16), no padding; the
+// 16 pieces of 16 bytes of row r are stored in the order c ^ (r % 16), so the
+// operand reads of 16 lanes (16 rows, one piece) fall on 16 distinct bank
+// groups.
+constexpr int GG_XSTAGE = GG_BM * GG_BK * 2;   // 16 KB
+typedef __attribute__((address_space(3))) void* gg_lds_ptr;
+
+template <int N>
+__device__ __forceinline__ void gg_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Four 16-byte LDS reads (the A operands of one K slice), completed inside
+// the statement.  Issued as one asm block because the compiler, which cannot
+// tell these reads apart from the stages the direct-to-LDS loads are filling,
+// would otherwise wait for every load in flight before each of them.
+__device__ __forceinline__ void gg_lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                             u32x4g& r0, u32x4g& r1, u32x4g& r2, u32x4g& r3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// Workgroup barrier without the release fence of __syncthreads, which would
+// drain every load in flight (the direct-to-LDS loads count as LDS writes).
+// The caller has already waited for the LDS data the barrier publishes; the
+// wait for this wave's LDS instructions and the memory clobber keep LDS
+// accesses on their side of it.
+__device__ __forceinline__ void gg_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One tile.  WDT: weight format (MOE_I4 or MOE_BF16); DOWN: down projection
+// (else gate/up + SwiGLU); NW: K steps in flight; GUARD: the step count is
+// not a multiple of NW (the last group has idle steps).
+//
+// Streams.  Each step issues, in this order, the activation stage of step
+// kt + NW (direct global-to-LDS loads: 4 instructions per wave, each 4 rows
+// of 256 bytes) and the weights of step kt + NW (4 register loads per wave).
+// Before the barrier that opens step kt a wave waits until its own
+// activation loads of step kt have landed: younger than them are the weight
+// loads of step kt and everything issued in the NW - 1 steps since, so
+// "vmcnt <= 4 + 8 (NW - 1)" is that condition (vector memory completes in
+// issue order; bf16 weights are 16 loads per step, not 4).  The compiler's
+// own waits cover the weight registers.  With
+// NW + 1 activation buffers, the stage overwritten at step kt was read at
+// step kt - 1, before that step's closing barrier.
+//
+// QUAD (int4, K steps a multiple of 4): weights are loaded by quads of 4 K
+// steps, 64 contiguous bytes per lane (4 back-to-back instructions covering
+// 256 contiguous bytes of each row), so that each row is read in runs that
+// keep its DRAM page open; one 16-byte piece of the quad feeds each step.
+// The K order inside a quad follows: step s of quad q takes, for lane group
+// kg, the codes q * 512 + kg * 128 + 32 s + [0, 32), and the activation
+// stages gather the same positions.  NW is then 8 (two quads in flight).
+template <int WDT, bool DOWN, int NW, bool GUARD, bool QUAD>
+__device__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+  constexpr bool I4 = WDT == MOE_I4;
+  static_assert(!QUAD || (I4 && NW == 8), "quads: int4, two in flight");
+  constexpr int NB = NW + 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, kg = lane >> 4;
+  const ExpertSetDev& ws = t.shared ? a.ws : a.w;
+  const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
+  const int rows = DOWN ? a.H : (t.shared ? a.Is : a.I);   // gate/up: rows of each half
+  const uint8_t* W = DOWN ? ws.dn + (int64_t)t.e * ws.dn_stride : ws.gu + (int64_t)t.e * ws.gu_stride;
+  const float* S = reinterpret_cast<const float*>(DOWN ? ws.dns + (int64_t)t.e * ws.dns_stride
+                                                        : ws.gus + (int64_t)t.e * ws.gus_stride);
+  const int64_t rowb = I4 ? K / 2 : (int64_t)K * 2;
+
+  // the wave's weight rows: N-subtile ns, lane row ln
+  int64_t wrow[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    if (DOWN) {
+      wrow[ns] = (int64_t)t.nt * 256 + wave * GG_NW + ns * 16 + ln;
+    } else {
+      const int c = t.nt * 128 + wave * 32 + (ns & 1) * 16 + ln;
+      wrow[ns] = ns < 2 ? c : rows + c;
+    }
+  }
+  const uint8_t* wp[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) wp[ns] = W + wrow[ns] * rowb;
+
+  // Per-tile row data for the epilogue, loaded first so that its latency
+  // overlaps the K loop: the lane's four weight-row scales (registers), and
+  // per tile row the output row index and, for int4, the activation row sum
+  // (LDS, written after the K-loop prologue has issued its loads).
+  float sc[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) sc[ns] = I4 ? S[wrow[ns]] : 1.0f;
+  int32_t* s_row = reinterpret_cast<int32_t*>(lds + NB * GG_XSTAGE);
+  float* s_rs = reinterpret_cast<float*>(s_row + GG_BM);
+  int meta_row = 0;
+  float meta_rs = 0.f;
+  if (threadIdx.x < GG_BM) {
+    const int r = min((int)threadIdx.x, t.n - 1);
+    const int pos = t.p0 + r;
+    if (DOWN) {
+      meta_row = t.shared ? pos : a.entries[pos];
+      if (I4) meta_rs = t.shared ? a.rs_hs[pos] : a.rs_h[pos];
+    } else {
+      meta_row = pos;
+      if (I4) meta_rs = a.rs_x[t.shared ? pos : a.entries[pos] / a.top_k];
+    }
+  }
+
+  // Activation rows of this wave's DMA: instruction i covers tile rows
+  // 16 wave + 4 i .. + 3; lane -> row 16 wave + 4 i + lane / 16, stored
+  // position lane % 16, which holds logical piece (lane % 16) ^ (row % 16).
+  // int4 weights pair nibbles (j, j + 4), so their activations are read from
+  // rows stored in the matching order (x_p, and h as gate/up writes it).
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = wave * 16 + i * 4 + (lane >> 4);
+    const int rr = min(r, t.n - 1);
+    const uint16_t* row;
+    if (DOWN) {
+      row = (t.shared ? a.h_s : a.h) + (int64_t)(t.p0 + rr) * K;
+    } else {
+      const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
+      row = (I4 ? a.x_p : a.x) + (int64_t)tok * K;
+    }
+    const int c = (lane & 15) ^ (r & 15);   // logical piece
+    xsrc[i] = reinterpret_cast<const uint8_t*>(row) +
+              (QUAD ? (c >> 2) * 256 + (c & 3) * 16 : 16 * c);
+  }
+  // the activation stage of step kt (quads: step kt = 4 q + s)
+  auto load_x = [&](int kt, int buf) {
+    const int64_t off = QUAD ? (int64_t)(kt >> 2) * 1024 + (kt & 3) * 64 : (int64_t)kt * (GG_BK * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(
+          xsrc[i] + off,
+          (gg_lds_ptr)(lds + buf * GG_XSTAGE + (wave * 16 + i * 4) * (GG_BK * 2)), 16, 0, 0);
+  };
+  // weights: per step, int4 16 bytes per N-subtile, bf16 64 bytes; per quad
+  // (QUAD), 64 bytes per N-subtile
+  constexpr int WV = QUAD ? 4 : (I4 ? 1 : 4);
+  auto load_w = [&](int kt, u32x4g (&v)[4][WV]) {
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+      for (int i = 0; i < WV; ++i) {
+        const int64_t off = QUAD ? (int64_t)(kt >> 2) * 256 + kg * 64 + i * 16
+                            : I4 ? (int64_t)kt * 64 + kg * 16
+                                 : (int64_t)kt * 256 + kg * 64 + i * 16;
+        // ordinary (cached) loads: the m-tiles of an expert re-read these
+        // rows and find them in L2
+        v[ns][i] = *reinterpret_cast<const u32x4g*>(wp[ns] + off);
+      }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The loop is unrolled by NW so that every weight stage has a fixed
+  // register name; all loads are unconditional (steps past the end repeat
+  // the last one) and, without GUARD, the body has no branches.
+  const int nk = K / GG_BK;
+  const uint32_t lds_base =
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds);
+  // weight register stages: one per step, or one per quad
+  constexpr int NWB = QUAD ? NW / 4 : NW;
+  u32x4g wbuf[NWB][4][WV];
+#pragma unroll
+  for (int st = 0; st < NW; ++st) {
+    load_x(min(st, nk - 1), st);
+    if (!QUAD) load_w(min(st, nk - 1), wbuf[st]);
+    else if ((st & 3) == 3) load_w(min(st, nk - 1), wbuf[st >> 2]);
+  }
+  if (threadIdx.x < GG_BM) {
+    s_row[threadIdx.x] = meta_row;
+    s_rs[threadIdx.x] = meta_rs;
+  }
+
+  for (int kt0 = 0; kt0 < nk; kt0 += NW) {
+#pragma unroll
+    for (int st = 0; st < NW; ++st) {
+      const int kt = kt0 + st;
+      // younger than this step's activation loads: per step 4 activation
+      // loads, plus the weight loads of each step (or of each quad's last
+      // step) since; QUAD: 7 steps x 4 + 2 quads x 16
+      gg_wait_vmcnt<QUAD ? 7 * 4 + 2 * 16 : 4 * WV + (NW - 1) * (4 + 4 * WV)>();
+      gg_barrier();
+      const uint32_t xb_lds = lds_base + (kt % NB) * GG_XSTAGE;
+      // pin this stage's weights here: without it the compiler hoists the
+      // conversions of all stages to the top of the group, waiting there for
+      // every load in flight
+      const int wsl = QUAD ? (st >> 2) : st;   // weight stage of this step
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns)
+#pragma unroll
+        for (int i = 0; i < WV; ++i) {
+          if (!QUAD || i == (st & 3)) asm volatile("" : "+v"(wbuf[wsl][ns][i]));
+        }
+      if (!GUARD || kt < nk) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          bf16x8 av[4];
+          {
+            const uint32_t base = xb_lds + ln * (GG_BK * 2) + 16 * ((kg * 4 + d) ^ ln);
+            u32x4g r0, r1, r2, r3;
+            gg_lds_read4(base, base + 16 * GG_BK * 2, base + 32 * GG_BK * 2, base + 48 * GG_BK * 2,
+                         r0, r1, r2, r3);
+            av[0] = as_bf16x8(r0);
+            av[1] = as_bf16x8(r1);
+            av[2] = as_bf16x8(r2);
+            av[3] = as_bf16x8(r3);
+          }
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) {
+            bf16x8 bv;
+            if constexpr (I4) {
+              const u32x4g wq = wbuf[wsl][ns][QUAD ? (st & 3) : 0];
+              const uint32_t w = d == 0 ? wq.x : d == 1 ? wq.y : d == 2 ? wq.z : wq.w;
+              bv = as_bf16x8(i4_to_bf16(w));
+            } else {
+              bv = as_bf16x8(wbuf[wsl][ns][d]);
+            }
+#pragma unroll
+            for (int ms = 0; ms < 4; ++ms)
+              acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ms], bv, acc[ms][ns], 0, 0, 0);
+          }
+        }
+      }
+      // refills: the activation stage of step kt + NW goes to the buffer
+      // read at step kt - 1 (free since this step's opening barrier)
+      load_x(min(kt + NW, nk - 1), (kt + NW) % NB);
+      if (!QUAD) load_w(min(kt + NW, nk - 1), wbuf[st]);
+      else if ((st & 3) == 3) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
+    }
+  }
+
+  // epilogue: lane holds rows m = 16 ms + 4 kg + j of column (weight row) ln
+  // of each N-subtile.  gate/up of int4 experts writes h in the order their
+  // down projection reads it (nibble pairs (j, j + 4) within groups of 8).
+  gg_wait_vmcnt<0>();
+  gg_barrier();
+  const float mul = I4 ? GG_DIV : 1.0f;
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = ms * 16 + kg * 4 + j;
+      if (m >= t.n) continue;
+      const float off = I4 ? GG_OFF * s_rs[m] : 0.f;
+      const int64_t orow = s_row[m];
+      if constexpr (DOWN) {
+        float* yrow = (t.shared ? a.y_s : a.y) + orow * a.H;
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) yrow[wrow[ns]] = sc[ns] * fmaf(mul, acc[ms][ns][j], -off);
+      } else {
+        uint16_t* hrow = (t.shared ? a.h_s : a.h) + orow * rows;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          const float g = sc[ns] * fmaf(mul, acc[ms][ns][j], -off);
+          const float u = sc[ns + 2] * fmaf(mul, acc[ms][ns + 2][j], -off);
+          const int64_t c = wrow[ns];
+          const int64_t pc = I4 ? (c & ~7) | ((c & 4) ? 2 * (c & 3) + 1 : 2 * (c & 3)) : c;
+          hrow[pc] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+        }
+      }
+    }
+  }
+}
+
+// K steps in flight: eight for int4 weights loaded by quads (64 registers per
+// quad), two for int4 K counts that are not a multiple of 4 and for bf16 (64
+// registers per step); the block runs one wave per SIMD, so the registers
+// and most of the LDS (nine activation stages) are its own.
+constexpr int GG_NW_I4 = 8, GG_NW_BF16 = 2;
+constexpr int GG_NB_MAX = GG_NW_I4 + 1;
+
+template <int WDT, bool DOWN>
+__device__ void gg_dispatch(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+  const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
+  const int nk = K / GG_BK;
+  if constexpr (WDT == MOE_I4) {
+    if (nk % 4 == 0) {
+      if (nk % 8 == 0) gg_run<WDT, DOWN, 8, false, true>(a, t, lds);
+      else gg_run<WDT, DOWN, 8, true, true>(a, t, lds);
+      return;
+    }
+    if (nk % 2 == 0) gg_run<WDT, DOWN, 2, false, false>(a, t, lds);
+    else gg_run<WDT, DOWN, 2, true, false>(a, t, lds);
+  } else {
+    if (nk % GG_NW_BF16 == 0) gg_run<WDT, DOWN, GG_NW_BF16, false, false>(a, t, lds);
+    else gg_run<WDT, DOWN, GG_NW_BF16, true, false>(a, t, lds);
+  }
+}
+
+template <int WR, int WS, bool DOWN>
+__global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ggemm(GgArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_NB_MAX * GG_XSTAGE + 2 * GG_BM * 4];
+  GgTile t;
+  if (!gg_tile(a, t)) return;
+  if (t.shared)
+    gg_dispatch<WS, DOWN>(a, t, lds);
+  else
+    gg_dispatch<WR, DOWN>(a, t, lds);
+}
+
+// Tiles of the buckets: active experts in order, ceil(count / 64) tiles each.
+__global__ __launch_bounds__(256) void k_make_tiles(const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ active,
+                                                    const int32_t* __restrict__ n_active,
+                                                    int32_t* __restrict__ tile_e,
+                                                    int32_t* __restrict__ tile_p0,
+                                                    int32_t* __restrict__ tile_n,
+                                                    int32_t* __restrict__ tile_first,
+                                                    int32_t* __restrict__ tile_cnt,
+                                                    int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t scan[kMaxExperts];
+  const int na = *n_active;
+  for (int s = threadIdx.x; s < na; s += 256) {
+    const int e = active[s];
+    scan[s] = (offsets[e + 1] - offsets[e] + GG_BM - 1) / GG_BM;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int s = 0; s < na; ++s) {
+      const int c = scan[s];
+      scan[s] = run;
+      run += c;
+    }
+    *n_tiles = run;
+  }
+  __syncthreads();
+  for (int s = threadIdx.x; s < na; s += 256) {
+    const int e = active[s];
+    const int p = offsets[e], cnt = offsets[e + 1] - p;
+    const int ntile = (cnt + GG_BM - 1) / GG_BM;
+    for (int i = 0, q = scan[s]; i < ntile; ++i, ++q) {
+      tile_e[q] = e;
+      tile_p0[q] = p + i * GG_BM;
+      tile_n[q] = min(GG_BM, cnt - i * GG_BM);
+      tile_first[q] = scan[s];
+      tile_cnt[q] = ntile;
+    }
+  }
+}
+
+// Row sums (fp32) of bf16 rows, one wave per row; with perm, also a copy of
+// the rows with every group of 8 stored in the order 0,4,1,5,2,6,3,7 (the
+// activation order int4 tiles read).
+__global__ __launch_bounds__(256) void k_rowsum_bf16(const uint16_t* __restrict__ rows, int32_t n,
+                                                     int32_t K, float* __restrict__ out,
+                                                     uint16_t* __restrict__ perm) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= n) return;
+  const uint16_t* p = rows + r * K;
+  float s = 0.f;
+  for (int c = lane * 8; c < K; c += 512) {
+    const u32x4g v = *reinterpret_cast<const u32x4g*>(p + c);
+    if (perm) *reinterpret_cast<u32x4g*>(perm + r * K + c) = perm_0415(v);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) s += __uint_as_float(w[d] << 16) + __uint_as_float(w[d] & 0xFFFF0000u);
+  }
+  s = wave_sum(s);
+  if (lane == 0) out[r] = s;
+}
+
+hipError_t launch_rowsum_bf16(const uint16_t* rows, int32_t n, int32_t K, float* out,
+                              uint16_t* perm, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rowsum_bf16, dim3((n + 3) / 4), dim3(256), 0, s, rows, n, K, out, perm);
+  return hipGetLastError();
+}
+
+bool ggemm_supported(const moe_layer_desc& d) {
+  const bool fmt = (d.expert_dtype == MOE_I4 || d.expert_dtype == MOE_BF16) &&
+                   (d.n_shared == 0 || d.shared_dtype == MOE_I4 || d.shared_dtype == MOE_BF16);
+  const int64_t Is = (int64_t)d.inter * (d.n_shared > 0 ? d.n_shared : 1);
+  return fmt && d.act_dtype == MOE_BF16 && d.hidden % 256 == 0 && d.inter % 128 == 0 &&
+         Is % 128 == 0 && d.n_experts <= kMaxExperts;
+}
+
+int32_t ggemm_max_tiles(int32_t T, int32_t K, int32_t E) {
+  const int64_t slots = (int64_t)T * K;
+  const int64_t tiles = (slots + GG_BM - 1) / GG_BM + (slots < E ? slots : E);
+  return (int32_t)tiles;
+}
+
+hipError_t launch_make_tiles(const int32_t* offsets, const int32_t* active, const int32_t* n_active,
+                             int32_t* tile_e, int32_t* tile_p0, int32_t* tile_n,
+                             int32_t* tile_first, int32_t* tile_cnt, int32_t* n_tiles,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_make_tiles, dim3(1), dim3(256), 0, s, offsets, active, n_active, tile_e,
+                     tile_p0, tile_n, tile_first, tile_cnt, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_ggemm(GgArgs a, bool down, int dtype, int shared_dtype, hipStream_t s) {
+  a.nt_r = down ? a.H / 256 : a.I / 128;
+  a.nt_s = a.has_shared ? (down ? a.H / 256 : a.Is / 128) : 0;
+  a.s_tiles = a.has_shared ? (a.T + GG_BM - 1) / GG_BM : 0;
+  if (!a.has_shared) shared_dtype = dtype;
+  const int64_t total = (int64_t)a.max_tiles * a.nt_r + (int64_t)a.s_tiles * a.nt_s;
+  if (total <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+#define GG_GO(WR, WS, DN) \
+  hipLaunchKernelGGL((k_ggemm<WR, WS, DN>), dim3(blocks), dim3(GG_THREADS), 0, s, a)
+  const bool r4 = dtype == MOE_I4, s4 = shared_dtype == MOE_I4;
+  if (down) {
+    if (r4 && s4) GG_GO(MOE_I4, MOE_I4, true);
+    else if (r4) GG_GO(MOE_I4, MOE_BF16, true);
+    else if (s4) GG_GO(MOE_BF16, MOE_I4, true);
+    else GG_GO(MOE_BF16, MOE_BF16, true);
+  } else {
+    if (r4 && s4) GG_GO(MOE_I4, MOE_I4, false);
+    else if (r4) GG_GO(MOE_I4, MOE_BF16, false);
+    else if (s4) GG_GO(MOE_BF16, MOE_I4, false);
+    else GG_GO(MOE_BF16, MOE_BF16, false);
+  }
+#undef GG_GO
+  return hipGetLastError();
+}
+
+}  // namespace moe

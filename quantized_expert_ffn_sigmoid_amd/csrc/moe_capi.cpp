@@ -24,6 +24,17 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool dtype_is_weight(int32_t t) { return t == MOE_I4 || t == MOE_I2 || t == MOE_BF16; }
 
 // Descriptor consistency (MOE_EINVAL) and kernel coverage (MOE_EUNSUPPORTED).
+// The decode-sized expert path (GEMV kernels) covers the layer's shapes.
+bool gemv_layer_ok(const moe_layer_desc& d) {
+  if (!gemv_supported(d.expert_dtype, d.hidden) || !gemv_supported(d.expert_dtype, d.inter))
+    return false;
+  if (d.n_shared > 0 &&
+      (!gemv_pair_supported(d.expert_dtype, d.hidden, d.shared_dtype, d.hidden) ||
+       !gemv_pair_supported(d.expert_dtype, d.inter, d.shared_dtype, d.inter * d.n_shared)))
+    return false;
+  return true;
+}
+
 moe_status check_desc(const moe_layer_desc* d) {
   if (!d) return MOE_EINVAL;
   if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
@@ -43,12 +54,9 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (d->router == MOE_ROUTER_SIGMOID_NOAUX_TC && d->n_group > 64) return MOE_EUNSUPPORTED;
   if (d->hidden % 32 != 0) return MOE_EUNSUPPORTED;
-  if (!gemv_supported(d->expert_dtype, d->hidden) || !gemv_supported(d->expert_dtype, d->inter))
-    return MOE_EUNSUPPORTED;
-  if (d->n_shared > 0 &&
-      (!gemv_pair_supported(d->expert_dtype, d->hidden, d->shared_dtype, d->hidden) ||
-       !gemv_pair_supported(d->expert_dtype, d->inter, d->shared_dtype, d->inter * d->n_shared)))
-    return MOE_EUNSUPPORTED;
+  // a layer is accepted when either expert path covers it; calls whose batch
+  // size selects an uncovered path fail with MOE_EUNSUPPORTED
+  if (!gemv_layer_ok(*d) && !ggemm_supported(*d)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -85,7 +93,7 @@ int32_t epg_of(int32_t dtype) { return dtype == MOE_BF16 ? 8 : 32; }
 // Workspace carve for n tokens.  Every region is 256-byte aligned.
 struct Carve {
   size_t z, idx, w, counts, offsets, entries, inverse, active, n_active, h, h_sh, Y, S, xn, yl,
-      xs, xs_sh, total;
+      xs, xs_sh, tiles, rs, xp, total;
 };
 
 Carve carve(const moe_layer_desc& d, int64_t T) {
@@ -115,6 +123,9 @@ Carve carve(const moe_layer_desc& d, int64_t T) {
   c.yl = take(sizeof(float) * T * H);
   c.xs = take(sizeof(float) * T * H);
   c.xs_sh = take(sizeof(float) * T * H);
+  c.tiles = take(sizeof(int32_t) * (5 * (size_t)ggemm_max_tiles((int32_t)T, (int32_t)K, (int32_t)E) + 1));
+  c.rs = take(sizeof(float) * (size_t)T * (K + 2));
+  c.xp = take(sizeof(uint16_t) * (size_t)T * H);
   c.total = o;
   return c;
 }
@@ -174,8 +185,10 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   void* xs = at<void>(ws, c.xs);
   void* xs_sh = epg_s && epg_s != epg_r ? at<void>(ws, c.xs_sh) : xs;
 
+  const bool use_gg = T > kDecodeTokens && ggemm_supported(d);
+  if (!use_gg && !gemv_layer_ok(d)) return MOE_EUNSUPPORTED;
   SliceReq sr{};
-  if (gu_ring) {
+  if (gu_ring && !use_gg) {
     sr.epg_a = epg_r;
     sr.dst_a = xs;
     if (xs_sh != xs) {
@@ -198,6 +211,56 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   if (!fused_route)
     MOE_TRY(launch_bucket(T, K, E, idx, counts, offsets, entries, inverse, active, n_active, s));
   record(opts, MOE_STAGE_BUCKET, 1, s);
+
+  if (use_gg) {
+    // prefill-sized buckets: grouped GEMM on the matrix cores
+    const int32_t mt = ggemm_max_tiles(T, K, E);
+    int32_t* tiles = at<int32_t>(ws, c.tiles);
+    GgArgs q{};
+    q.w = dev_set(w.routed);
+    if (has_sh) q.ws = dev_set(w.shared);
+    q.has_shared = has_sh;
+    q.H = H;
+    q.I = I;
+    q.Is = Ish;
+    q.T = T;
+    q.top_k = K;
+    q.entries = entries;
+    q.tile_e = tiles;
+    q.tile_p0 = tiles + mt;
+    q.tile_n = tiles + 2 * mt;
+    q.tile_first = tiles + 3 * mt;
+    q.tile_cnt = tiles + 4 * mt;
+    q.n_tiles = tiles + 5 * mt;
+    q.max_tiles = mt;
+    q.x = static_cast<const uint16_t*>(x);
+    q.h = static_cast<uint16_t*>(h);
+    q.h_s = static_cast<uint16_t*>(h_sh);
+    q.y = Y;
+    q.y_s = S;
+    float* rs = at<float>(ws, c.rs);
+    q.rs_x = rs;
+    q.rs_h = rs + T;
+    q.rs_hs = rs + (int64_t)T * (K + 1);
+    const bool any_i4 = d.expert_dtype == MOE_I4 || (has_sh && d.shared_dtype == MOE_I4);
+    MOE_TRY(launch_make_tiles(offsets, active, n_active, tiles, tiles + mt, tiles + 2 * mt,
+                              tiles + 3 * mt, tiles + 4 * mt, tiles + 5 * mt, s));
+    record(opts, MOE_STAGE_GATE_UP, 0, s);
+    q.x_p = at<uint16_t>(ws, c.xp);
+    if (any_i4) MOE_TRY(launch_rowsum_bf16(q.x, T, H, rs, at<uint16_t>(ws, c.xp), s));
+    MOE_TRY(launch_ggemm(q, false, d.expert_dtype, d.shared_dtype, s));
+    record(opts, MOE_STAGE_GATE_UP, 1, s);
+    record(opts, MOE_STAGE_DOWN, 0, s);
+    if (d.expert_dtype == MOE_I4) MOE_TRY(launch_rowsum_bf16(q.h, T * K, I, rs + T, nullptr, s));
+    if (has_sh && d.shared_dtype == MOE_I4)
+      MOE_TRY(launch_rowsum_bf16(q.h_s, T, Ish, rs + (int64_t)T * (K + 1), nullptr, s));
+    MOE_TRY(launch_ggemm(q, true, d.expert_dtype, d.shared_dtype, s));
+    record(opts, MOE_STAGE_DOWN, 1, s);
+    record(opts, MOE_STAGE_COMBINE, 0, s);
+    MOE_TRY(launch_combine(Y, tw, has_sh ? S : nullptr, T, K, H, residual, out, y_copy, s));
+    record(opts, MOE_STAGE_COMBINE, 1, s);
+    return MOE_OK;
+  }
 
   GemvArgs g{};
   g.w = dev_set(w.routed);
@@ -316,6 +379,7 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, in
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int32_t I = shared ? d->inter * d->n_shared : d->inter;
   const int act_bf16 = d->act_dtype == MOE_BF16;
+  if (!gemv_supported(dtype, d->hidden) || !gemv_supported(dtype, I)) return MOE_EUNSUPPORTED;
   GemvArgs g{};
   g.w = dev_set(*set);
   g.src.routed = 0;

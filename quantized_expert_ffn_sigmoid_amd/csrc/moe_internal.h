@@ -98,6 +98,36 @@ struct GemvArgs {
   int32_t rb, nb, rb_s, nb_s;
 };
 
+// One grouped-GEMM launch (prefill-sized buckets, bf16 activations): the
+// routed tiles of the buckets and, optionally, the shared expert's token rows.
+struct GgArgs {
+  ExpertSetDev w, ws;
+  int32_t has_shared, H, I, Is, T, top_k;
+  const int32_t* entries;    // bucket entries (flat slot f = t * top_k + j)
+  const int32_t* tile_e;     // routed m-tiles: expert, first bucket position, rows
+  const int32_t* tile_p0;
+  const int32_t* tile_n;
+  const int32_t* tile_first; // first m-tile of the tile's expert, and its count
+  const int32_t* tile_cnt;
+  const int32_t* n_tiles;    // routed m-tiles in use (device)
+  int32_t max_tiles;         // routed m-tiles in the grid
+  const uint16_t* x;         // [T][H] bf16
+  const uint16_t* x_p;       // x with each group of 8 in the order 0,4,1,5,2,6,3,7
+                             // (read by int4 experts; h of int4 experts is
+                             // written in that order too)
+  uint16_t* h;               // [bucket position][I] bf16
+  uint16_t* h_s;             // [T][Is] bf16
+  float* y;                  // [slot f][H]
+  float* y_s;                // [T][H]
+  // fp32 row sums of the bf16 activation rows of int4 experts (the int4
+  // operand carries an offset that the epilogue removes with them)
+  const float* rs_x;         // [T]       rows of x
+  const float* rs_h;         // [T * k]   rows of h
+  const float* rs_hs;        // [T]       rows of the shared expert's h
+  // filled in by the launcher
+  int32_t s_tiles, nt_r, nt_s;
+};
+
 // ------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Shapes are validated by the
 // caller (moe_capi.cpp).
@@ -145,6 +175,18 @@ hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, i
 hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);
+
+// Grouped GEMM: whether a layer qualifies, the routed m-tile bound for T
+// tokens, the tile list from the buckets, and the launch.
+bool ggemm_supported(const moe_layer_desc& d);
+int32_t ggemm_max_tiles(int32_t T, int32_t K, int32_t E);
+hipError_t launch_make_tiles(const int32_t* offsets, const int32_t* active, const int32_t* n_active,
+                             int32_t* tile_e, int32_t* tile_p0, int32_t* tile_n,
+                             int32_t* tile_first, int32_t* tile_cnt, int32_t* n_tiles,
+                             hipStream_t s);
+hipError_t launch_ggemm(GgArgs a, bool down, int dtype, int shared_dtype, hipStream_t s);
+hipError_t launch_rowsum_bf16(const uint16_t* rows, int32_t n, int32_t K, float* out,
+                              uint16_t* perm, hipStream_t s);
 
 // Whether the GEMV kernels cover an input length K of this dtype: K must be
 // a whole number of 64-granule chunks, or a power-of-two number of granules
