@@ -589,18 +589,51 @@ struct BlockWork {
   int e, p0, nrows, rb_index;
 };
 
+// Logical id of block b of n such that the blocks the hardware deals to one
+// XCD (b mod 8) take consecutive logical ids.
+__device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t n) {
+  const int64_t q = n >> 3, r = n & 7, x = b & 7;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (b >> 3);
+}
+
 __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
-  const int64_t bid = blockIdx.x;
   const int64_t routed_blocks = (int64_t)a.n_slots * a.nb;
-  const int64_t nblk = routed_blocks + a.nb_s;
-  const int64_t before = bid * a.nb_s / nblk;           // shared blocks before bid
-  const bool is_shared = (bid + 1) * a.nb_s / nblk > before;
+  const int64_t shared_blocks = (int64_t)a.nb_s * a.ntg_s;
+  const int64_t nblk = routed_blocks + shared_blocks;
+  // token mode: the blocks that read the same weight rows for different tokens
+  // sit next to each other on one XCD, so the rows come from HBM once
+  const int64_t bid = a.per_token ? xcd_logical(blockIdx.x, nblk) : (int64_t)blockIdx.x;
+  const int64_t before = bid * shared_blocks / nblk;       // shared blocks before bid
+  const bool is_shared = (bid + 1) * shared_blocks / nblk > before;
+  const RowSource& src = a.src;
   if (!is_shared) {
-    const int rbid = (int)(bid - before);
-    const int slot = rbid / a.nb;
+    const int64_t rbid = bid - before;
     bw.shared = false;
-    bw.rb_index = rbid - slot * a.nb;
-    const RowSource& src = a.src;
+    if (a.per_token) {
+      const int p = (int)(rbid % a.n_slots);
+      bw.rb_index = (int)(rbid / a.n_slots);
+      bw.p0 = p;
+      bw.nrows = 1;
+      if (src.routed) {
+        // the active expert whose bucket holds position p (buckets are
+        // contiguous and ascending with the active list)
+        const int na = *src.n_active;
+        if (na <= 0) return false;
+        int lo = 0, hi = na - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (src.offsets[src.active[mid]] <= p) lo = mid; else hi = mid - 1;
+        }
+        bw.e = src.active[lo];
+        if (p >= src.offsets[bw.e + 1]) return false;
+      } else {
+        bw.e = src.fixed_expert;
+        if (p >= src.n_rows) return false;
+      }
+      return true;
+    }
+    const int slot = (int)(rbid / a.nb);
+    bw.rb_index = (int)(rbid - (int64_t)slot * a.nb);
     if (src.routed) {
       if (slot >= *src.n_active) return false;
       bw.e = src.active[slot];
@@ -613,10 +646,11 @@ __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
     }
   } else {
     bw.shared = true;
-    bw.rb_index = (int)before;
+    const int tg = (int)(before % a.ntg_s);
+    bw.rb_index = (int)(before / a.ntg_s);
     bw.e = 0;
-    bw.p0 = 0;
-    bw.nrows = a.n_tok;
+    bw.p0 = tg * a.tok_s;
+    bw.nrows = min(a.tok_s, a.n_tok - bw.p0);
   }
   return bw.nrows > 0;
 }
@@ -669,16 +703,17 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
 #pragma unroll
     for (int n = 0; n < NTMAX; ++n) {
       const int i = i0 + (n < nt ? n : 0);
+      const int q = bw.p0 + i;   // bucket position, fixed-expert row or token
       if (DOWN) {
-        xo[n] = ((int64_t)bw.p0 + i) * jb.K;
-        dr[n] = (!bw.shared && src.routed) ? (int64_t)src.entries[bw.p0 + i] : (int64_t)i;
+        xo[n] = (int64_t)q * jb.K;
+        dr[n] = (!bw.shared && src.routed) ? (int64_t)src.entries[q] : (int64_t)q;
       } else {
         int t;
-        if (bw.shared) t = i;
-        else if (src.routed) t = src.entries[bw.p0 + i] / src.top_k;
-        else t = src.rows ? src.rows[i] / src.row_div : i;
+        if (bw.shared) t = q;
+        else if (src.routed) t = src.entries[q] / src.top_k;
+        else t = src.rows ? src.rows[q] / src.row_div : q;
         xo[n] = (int64_t)t * jb.K;
-        dr[n] = (int64_t)bw.p0 + i;
+        dr[n] = q;
       }
     }
     if constexpr (kRingFmt) {
@@ -722,7 +757,8 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
 
 // ------------------------------------------------------------------ kernels
 // One launch covers the routed experts (n_slots x nb blocks; slots beyond
-// n_active exit at once) and, optionally, the shared expert (nb_s blocks).
+// n_active, or beyond the bucketed rows in token mode, exit at once) and,
+// optionally, the shared expert (nb_s x ntg_s blocks).
 
 template <int WR, int KR, int WS, int KS, int NTMAX, int ABF16, bool DOWN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_gemv(GemvArgs a) {

@@ -86,12 +86,26 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     a.geo_s = a.geo;
     shared_dtype = dtype;
   }
+  // tokens one pass of the kernel takes (two only on short slices, where the
+  // second token's activations fit in registers); buckets that may hold more
+  // switch the launch to token mode, which splits them over blocks instead of
+  // making one block pass over its rows again
+  const int ntmax = (a.geo.kc <= 32 && max_rows_per_slot >= 2) ? 2 : 1;
+  a.per_token = max_rows_per_slot > ntmax;
+  if (a.per_token) {
+    a.n_slots = a.src.routed ? a.n_tok * a.src.top_k : a.src.n_rows;
+    a.tok_s = ntmax;
+    a.ntg_s = (a.n_tok + ntmax - 1) / ntmax;
+  } else {
+    a.tok_s = a.n_tok;
+    a.ntg_s = 1;
+  }
   // bytes the launch streams (routed slots bounded by n_slots), split evenly
   // over the waves of one resident round; blocks whose rows are rounded up
   // must not spill into a second round, so grow the share until they fit
   const int64_t mat = row_bytes_of(dtype, kin, !down) * rows;
   const int64_t mat_s = a.has_shared ? row_bytes_of(shared_dtype, kin_s, !down) * rows_s : 0;
-  int64_t per_wave = ((int64_t)a.n_slots * mat + mat_s) / kTargetWaves;
+  int64_t per_wave = ((int64_t)a.n_slots * mat + (int64_t)a.ntg_s * mat_s) / kTargetWaves;
   if (per_wave < kMinBytesPerWave) per_wave = kMinBytesPerWave;
   int nb_s = 0;
   long long blocks = 0;
@@ -101,13 +115,12 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     a.nb = (rows + a.rb - 1) / a.rb;
     a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave) : 1;
     nb_s = a.has_shared ? (rows_s + a.rb_s - 1) / a.rb_s : 0;
-    blocks = (long long)a.n_slots * a.nb + nb_s;
+    blocks = (long long)a.n_slots * a.nb + (long long)nb_s * a.ntg_s;
     if (blocks <= kTargetBlocks) break;
     per_wave += per_wave / 16 + 1;
   }
   a.nb_s = nb_s;
   if (blocks <= 0 || max_rows_per_slot <= 0) return hipSuccess;
-  const int ntmax = max_rows_per_slot >= 2 ? 2 : 1;
   const unsigned nblk = (unsigned)blocks;
   switch (dtype) {
     case MOE_I4: return (down ? gemv_i4_dn : gemv_i4_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);

@@ -96,6 +96,12 @@ struct GemvArgs {
   // filled in by the launcher
   MatGeo geo, geo_s;
   int32_t rb, nb, rb_s, nb_s;
+  // Token mode, for buckets with more rows than one pass of the kernel takes:
+  // routed slots are bucket positions (one token of one expert per block) and
+  // the shared expert's row blocks are repeated for ntg_s groups of tok_s
+  // tokens, so that no block makes a second pass over its weight rows.
+  // Otherwise routed slots are active experts and ntg_s = 1, tok_s = n_tok.
+  int32_t per_token, tok_s, ntg_s;
 };
 
 // One grouped-GEMM launch (prefill-sized buckets, bf16 activations): the
