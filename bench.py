@@ -47,6 +47,7 @@ import numpy as np  # noqa: E402
 import gen  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 METRIC = "MoE layer tokens/s + achieved HBM GB/s (int4 decode) at 1 MI355X"
 
 
@@ -59,6 +60,7 @@ class Hip:
         vp, P = ctypes.c_void_p, ctypes.POINTER
         L.hipEventCreate.argtypes = [P(vp)]
         L.hipEventElapsedTime.argtypes = [P(ctypes.c_float), vp, vp]
+        L.hipEventRecord.argtypes = [vp, vp]
         L.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
         L.hipStreamEndCapture.argtypes = [vp, P(vp)]
         L.hipGraphInstantiate.argtypes = [P(vp), vp, vp, vp, ctypes.c_size_t]
@@ -73,6 +75,9 @@ class Hip:
         e = ctypes.c_void_p()
         self._ok(self.L.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
         return e.value
+
+    def record(self, ev: int, stream: int):
+        self._ok(self.L.hipEventRecord(ev, stream), "hipEventRecord")
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
@@ -96,6 +101,39 @@ class Hip:
         self._ok(self.L.hipGraphLaunch(exe, stream), "hipGraphLaunch")
 
 
+# ------------------------------------------------ counter-measured traffic
+# HBM bytes per launch of the gate/up kernel on the default workload, from the
+# FETCH_SIZE and WRITE_SIZE counters (rocprofv3 --pmc, one pass each) scaled by
+# what the same counters read for a plain 1 GiB device copy.  The record holds
+# a digest of the sources that build and launch the kernel; once any of them
+# changes the counters no longer describe it and the traffic is reported null.
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemv_gate_up__glm_layer_decode_1tok.md")
+TRAFFIC_SOURCES = ["gemv_impl.h", "k_gemv.hip", "k_gemv_i4_gu.hip", "moe_internal.h",
+                   "moe_capi.cpp"]
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_expert_ffn_sigmoid_amd", "csrc")
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    if workload != "c2" or not os.path.exists(TRAFFIC_RECORD):
+        return None
+    with open(TRAFFIC_RECORD) as f:
+        for line in f:
+            if line.startswith("traffic-record: "):
+                rec = json.loads(line[len("traffic-record: "):])
+                if rec.get("sources_sha256") == kernel_sources_digest():
+                    return int(rec["bytes_per_launch"])
+    return None
+
+
 # ------------------------------------------------------- byte accounting
 def expert_bytes(cfg, dtype):
     return gen.expert_bytes(dtype, cfg.hidden, cfg.inter)
@@ -115,6 +153,15 @@ def gate_up_bytes(cfg, dtype, n_active, T):
         sb = gen.expert_bytes(cfg.shared_dtype, cfg.hidden, Is)
         b += sb["gate_up"] + (0 if cfg.shared_dtype == gen.BF16 else 4 * 2 * Is) + T * Is * act
     return b
+
+
+def gate_up_flops(cfg, T):
+    """Algorithmic flops of one gate/up launch: every (token, routed expert)
+    pair and every token through the shared expert, 2 flops per weight."""
+    f = 2.0 * T * cfg.top_k * 2 * cfg.inter * cfg.hidden
+    if cfg.n_shared:
+        f += 2.0 * T * 2 * cfg.inter * cfg.n_shared * cfg.hidden
+    return f
 
 
 def layer_bytes(cfg, dtype, n_active, T):
@@ -238,6 +285,8 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     stage_ids = list(range(capi.MOE_N_STAGES)) if args.stages else [capi.MOE_STAGE_GATE_UP]
     evs = [[[hip.event(), hip.event()] for _ in stage_ids] for _ in range(K)]
+    # an empty event pair per step: what an event bracket adds by itself
+    evp = [[hip.event(), hip.event()] for _ in range(K)]
 
     def step(i, timed):
         l, p = i % L, i % P
@@ -246,6 +295,8 @@ def main():
             events = [0] * (2 * capi.MOE_N_STAGES)
             for k, s in enumerate(stage_ids):
                 events[2 * s], events[2 * s + 1] = evs[i][k]
+            hip.record(evp[i][0], stream.cuda_stream)
+            hip.record(evp[i][1], stream.cuda_stream)
         capi.moe_layer_forward_ex(desc, weights[l], xs[p], T, out, None, None, ws, nb,
                                   stream=stream.cuda_stream, events=events)
 
@@ -286,10 +337,40 @@ def main():
     for k, s_id in enumerate(stage_ids):
         stage_ms[s_id] = [hip.elapsed_ms(evs[i][k][0], evs[i][k][1]) for i in range(K)]
     gu_ms = float(np.mean(stage_ms[capi.MOE_STAGE_GATE_UP]))
+    pair_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evp]))
     gu_bytes = float(np.mean([gate_up_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     lay_bytes = float(np.mean([layer_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
 
+    if base == "c3":
+        # prefill: the grouped GEMM on the matrix cores, priced in flops
+        flops = gate_up_flops(cfg, T)
+        tflops = flops / (gu_ms * 1e-3) / 1e12
+        roofline = {
+            "kernel": "moe::k_ggemm gate/up + SwiGLU (grouped GEMM, int4 routed + bf16 shared)",
+            "bound": "mfma",
+            "achieved": round(tflops, 1),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": int(flops),
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "event_pair_us": round(pair_ms * 1e3, 3),
+        }
+    else:
+        roofline = {
+            "kernel": "moe::k_gemv gate/up + SwiGLU (routed and shared experts)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(wl),
+            "bytes_per_launch": int(gu_bytes),
+            "avg_launch_us": round(gu_ms * 1e3, 3),
+            "event_pair_us": round(pair_ms * 1e3, 3),
+        }
     names = {capi.MOE_STAGE_ROUTE: "route", capi.MOE_STAGE_BUCKET: "bucket",
              capi.MOE_STAGE_GATE_UP: "gate_up", capi.MOE_STAGE_DOWN: "down",
              capi.MOE_STAGE_COMBINE: "combine"}
@@ -318,17 +399,7 @@ def main():
         },
         "layer_hbm_gbps": round(lay_bytes / (ms_step * 1e-3) / 1e9, 1),
         "layer_bytes_per_step": int(lay_bytes),
-        "roofline": {
-            "kernel": "expert gate/up + SwiGLU, routed and shared (k_gate_up)",
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "bytes_per_launch": int(gu_bytes),
-            "avg_launch_us": round(gu_ms * 1e3, 3),
-        },
+        "roofline": roofline,
     }
     if args.stages:
         res["stage_us"] = {names[s]: round(1e3 * float(np.mean(v)), 3) for s, v in stage_ms.items()}

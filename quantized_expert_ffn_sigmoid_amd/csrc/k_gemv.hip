@@ -56,16 +56,29 @@ static int64_t row_bytes_of(int dtype, int K, bool pair) {
   return (int64_t)K * bytes_x4 / 4 * (pair ? 2 : 1);
 }
 
-// Rows per block so that each wave streams about bytes_per_wave of codes
-// (whole passes of rpp rows).
+// Rows per block so that each of its waves streams about bytes_per_wave of
+// codes; a multiple of the rows one pass of a wave takes (the waves deal the
+// passes out round robin, so the last ones may take one pass fewer).
 static int rows_per_block(const MatGeo& g, int dtype, int K, int rows, bool pair,
                           int64_t bytes_per_wave) {
-  int64_t passes = bytes_per_wave / (row_bytes_of(dtype, K, pair) * g.rpp);
-  if (passes < 1) passes = 1;
-  int64_t rb = passes * kWaves * g.rpp;
-  if (rb > kMaxRingRows) rb = kMaxRingRows / (kWaves * g.rpp) * (kWaves * g.rpp);
+  int64_t units = bytes_per_wave * kWaves / (row_bytes_of(dtype, K, pair) * g.rpp);
+  if (units < 1) units = 1;
+  int64_t rb = units * g.rpp;
+  if (rb > kMaxRingRows) rb = kMaxRingRows / g.rpp * g.rpp;
   if (rb > rows) rb = rows;
   return (int)(rb < 1 ? 1 : rb);
+}
+
+// Relative time one byte of codes takes on a wave (x16).  An int4 byte holds
+// two elements and takes the unpack work; measured on the GLM decode layer
+// (int4 routed, bf16 shared), a bf16 byte streams in half the time, and
+// blocks sized by this weight finish together.
+static int64_t cost_per_byte(int dtype, int act_bf16) {
+  (void)act_bf16;
+  switch (dtype) {
+    case MOE_BF16: return 8;
+    default: return 16;
+  }
 }
 
 // Waves a launch aims for: 256 CUs x 8 resident waves (two 4-wave blocks per
@@ -100,20 +113,23 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     a.tok_s = a.n_tok;
     a.ntg_s = 1;
   }
-  // bytes the launch streams (routed slots bounded by n_slots), split evenly
-  // over the waves of one resident round; blocks whose rows are rounded up
-  // must not spill into a second round, so grow the share until they fit
+  // work of the launch (routed slots bounded by n_slots), in bytes weighted by
+  // the time a byte of each format takes, split evenly over the waves of one
+  // resident round; blocks whose rows are rounded up must not spill into a
+  // second round, so grow the share until they fit
   const int64_t mat = row_bytes_of(dtype, kin, !down) * rows;
   const int64_t mat_s = a.has_shared ? row_bytes_of(shared_dtype, kin_s, !down) * rows_s : 0;
-  int64_t per_wave = ((int64_t)a.n_slots * mat + (int64_t)a.ntg_s * mat_s) / kTargetWaves;
-  if (per_wave < kMinBytesPerWave) per_wave = kMinBytesPerWave;
+  const int64_t c_r = cost_per_byte(dtype, act_bf16), c_s = cost_per_byte(shared_dtype, act_bf16);
+  int64_t per_wave = ((int64_t)a.n_slots * mat * c_r + (int64_t)a.ntg_s * mat_s * c_s) /
+                     kTargetWaves;
+  if (per_wave < kMinBytesPerWave * c_r) per_wave = kMinBytesPerWave * c_r;
   int nb_s = 0;
   long long blocks = 0;
   // (nb_s is kept in a.nb_s for the kernel's block mapping)
   for (int it = 0; it < 64; ++it) {
-    a.rb = rows_per_block(a.geo, dtype, kin, rows, !down, per_wave);
+    a.rb = rows_per_block(a.geo, dtype, kin, rows, !down, per_wave / c_r);
     a.nb = (rows + a.rb - 1) / a.rb;
-    a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave) : 1;
+    a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave / c_s) : 1;
     nb_s = a.has_shared ? (rows_s + a.rb_s - 1) / a.rb_s : 0;
     blocks = (long long)a.n_slots * a.nb + (long long)nb_s * a.ntg_s;
     if (blocks <= kTargetBlocks) break;
