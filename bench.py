@@ -61,6 +61,7 @@ class Hip:
         L.hipEventCreate.argtypes = [P(vp)]
         L.hipEventElapsedTime.argtypes = [P(ctypes.c_float), vp, vp]
         L.hipEventRecord.argtypes = [vp, vp]
+        L.hipEventRecordWithFlags.argtypes = [vp, vp, ctypes.c_uint]
         L.hipStreamBeginCapture.argtypes = [vp, ctypes.c_int]
         L.hipStreamEndCapture.argtypes = [vp, P(vp)]
         L.hipGraphInstantiate.argtypes = [P(vp), vp, vp, vp, ctypes.c_size_t]
@@ -76,8 +77,13 @@ class Hip:
         self._ok(self.L.hipEventCreate(ctypes.byref(e)), "hipEventCreate")
         return e.value
 
-    def record(self, ev: int, stream: int):
-        self._ok(self.L.hipEventRecord(ev, stream), "hipEventRecord")
+    def record(self, ev: int, stream: int, captured: bool):
+        """Record ev on stream; inside a stream capture as an event-record
+        node (hipEventRecordExternal), which timestamps on every replay."""
+        if captured:
+            self._ok(self.L.hipEventRecordWithFlags(ev, stream, 1), "hipEventRecordWithFlags")
+        else:
+            self._ok(self.L.hipEventRecord(ev, stream), "hipEventRecord")
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
@@ -295,8 +301,8 @@ def main():
             events = [0] * (2 * capi.MOE_N_STAGES)
             for k, s in enumerate(stage_ids):
                 events[2 * s], events[2 * s + 1] = evs[i][k]
-            hip.record(evp[i][0], stream.cuda_stream)
-            hip.record(evp[i][1], stream.cuda_stream)
+            hip.record(evp[i][0], stream.cuda_stream, not args.eager)
+            hip.record(evp[i][1], stream.cuda_stream, not args.eager)
         capi.moe_layer_forward_ex(desc, weights[l], xs[p], T, out, None, None, ws, nb,
                                   stream=stream.cuda_stream, events=events)
 

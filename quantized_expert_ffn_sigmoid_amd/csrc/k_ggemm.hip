@@ -180,7 +180,7 @@ __device__ __forceinline__ void gg_barrier() {
 // kg, the codes q * 512 + kg * 128 + 32 s + [0, 32), and the activation
 // stages gather the same positions.  NW is then 8 (two quads in flight).
 template <int WDT, bool DOWN, int NW, bool GUARD, bool QUAD>
-__device__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+__device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   constexpr bool I4 = WDT == MOE_I4;
   static_assert(!QUAD || (I4 && NW == 8), "quads: int4, two in flight");
   constexpr int NB = NW + 1;
@@ -405,7 +405,7 @@ constexpr int GG_NW_I4 = 8, GG_NW_BF16 = 2;
 constexpr int GG_NB_MAX = GG_NW_I4 + 1;
 
 template <int WDT, bool DOWN>
-__device__ void gg_dispatch(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+__device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
   const int nk = K / GG_BK;
   if constexpr (WDT == MOE_I4) {
