@@ -52,13 +52,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4g v) { return __builtin_bit_cas
 // mantissa bits of 1.0, giving 1 + u / 16 = (24 + q) / 16 exactly; of the
 // exact encodings with an implicit leading one this has the smallest offset
 // relative to the code, which keeps the fp32 accumulation error small.
-__device__ __forceinline__ u32x4g i4_to_bf16(uint32_t w) {
+// The mask and the constant come in registers so that each register takes
+// one shift and one v_and_or_b32 (which cannot encode literal operands).
+__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ u32x4g i4_to_bf16(uint32_t w, uint32_t mask, uint32_t one) {
   const uint32_t u = w ^ 0x88888888u;
   u32x4g r;
-  r.x = ((u << 3) & 0x00780078u) | 0x3F803F80u;
-  r.y = ((u >> 1) & 0x00780078u) | 0x3F803F80u;
-  r.z = ((u >> 5) & 0x00780078u) | 0x3F803F80u;
-  r.w = ((u >> 9) & 0x00780078u) | 0x3F803F80u;
+  r.x = and_or(u << 3, mask, one);
+  r.y = and_or(u >> 1, mask, one);
+  r.z = and_or(u >> 5, mask, one);
+  r.w = and_or(u >> 9, mask, one);
   return r;
 }
 
@@ -120,20 +128,12 @@ __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
 // Activation stages in LDS: 64 rows x 256 bytes (128 bf16), no padding; the
 // 16 pieces of 16 bytes of row r are stored in the order c ^ (r % 16), so the
 // operand reads of 16 lanes (16 rows, one piece) fall on 16 distinct bank
-// groups.
+// groups.  Two stages: the one the step computes on and the one it fills.
 constexpr int GG_XSTAGE = GG_BM * GG_BK * 2;   // 16 KB
-typedef __attribute__((address_space(3))) void* gg_lds_ptr;
-
-template <int N>
-__device__ __forceinline__ void gg_wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
+constexpr int GG_XD = 4;                       // activation register sets in flight
 
 // Four 16-byte LDS reads (the A operands of one K slice), completed inside
-// the statement.  Issued as one asm block because the compiler, which cannot
-// tell these reads apart from the stages the direct-to-LDS loads are filling,
-// would otherwise wait for every load in flight before each of them.
+// the statement, so that the compiler places no wait of its own for them.
 __device__ __forceinline__ void gg_lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
                                              u32x4g& r0, u32x4g& r1, u32x4g& r2, u32x4g& r3) {
   asm volatile(
@@ -147,30 +147,24 @@ __device__ __forceinline__ void gg_lds_read4(uint32_t a0, uint32_t a1, uint32_t 
       : "memory");
 }
 
-// Workgroup barrier without the release fence of __syncthreads, which would
-// drain every load in flight (the direct-to-LDS loads count as LDS writes).
-// The caller has already waited for the LDS data the barrier publishes; the
-// wait for this wave's LDS instructions and the memory clobber keep LDS
-// accesses on their side of it.
+// Workgroup barrier after this wave's LDS writes have completed, without the
+// release fence of __syncthreads (which would also wait for every global load
+// in flight).  The memory clobber keeps LDS accesses on their side of it.
 __device__ __forceinline__ void gg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // One tile.  WDT: weight format (MOE_I4 or MOE_BF16); DOWN: down projection
-// (else gate/up + SwiGLU); NW: K steps in flight; GUARD: the step count is
-// not a multiple of NW (the last group has idle steps).
+// (else gate/up + SwiGLU); NW: K steps of weights in flight; GUARD: the step
+// count is not a multiple of the unroll (the last group has idle steps).
 //
-// Streams.  Each step issues, in this order, the activation stage of step
-// kt + NW (direct global-to-LDS loads: 4 instructions per wave, each 4 rows
-// of 256 bytes) and the weights of step kt + NW (4 register loads per wave).
-// Before the barrier that opens step kt a wave waits until its own
-// activation loads of step kt have landed: younger than them are the weight
-// loads of step kt and everything issued in the NW - 1 steps since, so
-// "vmcnt <= 4 + 8 (NW - 1)" is that condition (vector memory completes in
-// issue order; bf16 weights are 16 loads per step, not 4).  The compiler's
-// own waits cover the weight registers.  With
-// NW + 1 activation buffers, the stage overwritten at step kt was read at
-// step kt - 1, before that step's closing barrier.
+// Streams.  All global loads go to registers, so the compiler tracks each of
+// them and waits for exactly the ones an instruction needs (vector memory
+// completes in issue order).  Activations: the block loads step kt + 1 + GG_XD
+// into the register set freed by writing step kt + 1 to the LDS stage that
+// step kt + 1 computes on, so each activation tile has GG_XD steps to arrive.
+// Weights: step kt + NW (or its quad) is loaded into the registers step kt
+// has just consumed.
 //
 // QUAD (int4, K steps a multiple of 4): weights are loaded by quads of 4 K
 // steps, 64 contiguous bytes per lane (4 back-to-back instructions covering
@@ -183,7 +177,8 @@ template <int WDT, bool DOWN, int NW, bool GUARD, bool QUAD>
 __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   constexpr bool I4 = WDT == MOE_I4;
   static_assert(!QUAD || (I4 && NW == 8), "quads: int4, two in flight");
-  constexpr int NB = NW + 1;
+  constexpr int U = NW > GG_XD ? NW : GG_XD;   // unroll: whole register rotations
+  static_assert(U % NW == 0 && U % GG_XD == 0, "unroll covers both rotations");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, kg = lane >> 4;
@@ -213,11 +208,11 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // Per-tile row data for the epilogue, loaded first so that its latency
   // overlaps the K loop: the lane's four weight-row scales (registers), and
   // per tile row the output row index and, for int4, the activation row sum
-  // (LDS, written after the K-loop prologue has issued its loads).
+  // (LDS, published by the first barrier of the K loop).
   float sc[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) sc[ns] = I4 ? S[wrow[ns]] : 1.0f;
-  int32_t* s_row = reinterpret_cast<int32_t*>(lds + NB * GG_XSTAGE);
+  int32_t* s_row = reinterpret_cast<int32_t*>(lds + 2 * GG_XSTAGE);
   float* s_rs = reinterpret_cast<float*>(s_row + GG_BM);
   int meta_row = 0;
   float meta_rs = 0.f;
@@ -233,16 +228,17 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
     }
   }
 
-  // Activation rows of this wave's DMA: instruction i covers tile rows
-  // 16 wave + 4 i .. + 3; lane -> row 16 wave + 4 i + lane / 16, stored
-  // position lane % 16, which holds logical piece (lane % 16) ^ (row % 16).
-  // int4 weights pair nibbles (j, j + 4), so their activations are read from
-  // rows stored in the matching order (x_p, and h as gate/up writes it).
+  // Activation loads: thread (rb = tid / 16, p = tid % 16) moves stored
+  // position p of tile rows rb + 16 i (i < 4), which holds logical piece
+  // p ^ rb.  int4 weights pair nibbles (j, j + 4), so their activations are
+  // read from rows stored in the matching order (x_p, and h as gate/up writes
+  // it).
+  const int xp = threadIdx.x & 15, xrb = threadIdx.x >> 4;
+  const int xc = xp ^ xrb;   // logical piece
   const uint8_t* xsrc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = wave * 16 + i * 4 + (lane >> 4);
-    const int rr = min(r, t.n - 1);
+    const int rr = min(xrb + 16 * i, t.n - 1);
     const uint16_t* row;
     if (DOWN) {
       row = (t.shared ? a.h_s : a.h) + (int64_t)(t.p0 + rr) * K;
@@ -250,18 +246,21 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
       row = (I4 ? a.x_p : a.x) + (int64_t)tok * K;
     }
-    const int c = (lane & 15) ^ (r & 15);   // logical piece
     xsrc[i] = reinterpret_cast<const uint8_t*>(row) +
-              (QUAD ? (c >> 2) * 256 + (c & 3) * 16 : 16 * c);
+              (QUAD ? (xc >> 2) * 256 + (xc & 3) * 16 : 16 * xc);
   }
-  // the activation stage of step kt (quads: step kt = 4 q + s)
-  auto load_x = [&](int kt, int buf) {
+  const uint32_t lds_base =
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds);
+  const int nk = K / GG_BK;
+  auto load_x = [&](int kt, u32x4g (&v)[4]) {
     const int64_t off = QUAD ? (int64_t)(kt >> 2) * 1024 + (kt & 3) * 64 : (int64_t)kt * (GG_BK * 2);
 #pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4g*>(xsrc[i] + off);
+  };
+  auto store_x = [&](int buf, const u32x4g (&v)[4]) {
+#pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(
-          xsrc[i] + off,
-          (gg_lds_ptr)(lds + buf * GG_XSTAGE + (wave * 16 + i * 4) * (GG_BK * 2)), 16, 0, 0);
+      *reinterpret_cast<u32x4g*>(lds + buf * GG_XSTAGE + (xrb + 16 * i) * (GG_BK * 2) + xp * 16) = v[i];
   };
   // weights: per step, int4 16 bytes per N-subtile, bf16 64 bytes; per quad
   // (QUAD), 64 bytes per N-subtile
@@ -286,40 +285,43 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The loop is unrolled by NW so that every weight stage has a fixed
-  // register name; all loads are unconditional (steps past the end repeat
-  // the last one) and, without GUARD, the body has no branches.
-  const int nk = K / GG_BK;
-  const uint32_t lds_base =
-      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds);
-  // weight register stages: one per step, or one per quad
+  // prologue: activation sets of steps 0 .. GG_XD - 1, the first NW weight
+  // steps, step 0 into stage 0 and its register set refilled with step GG_XD
   constexpr int NWB = QUAD ? NW / 4 : NW;
+  u32x4g xr[GG_XD][4];
   u32x4g wbuf[NWB][4][WV];
 #pragma unroll
+  for (int j = 0; j < GG_XD; ++j) load_x(min(j, nk - 1), xr[j]);
+#pragma unroll
   for (int st = 0; st < NW; ++st) {
-    load_x(min(st, nk - 1), st);
     if (!QUAD) load_w(min(st, nk - 1), wbuf[st]);
     else if ((st & 3) == 3) load_w(min(st, nk - 1), wbuf[st >> 2]);
   }
+  store_x(0, xr[0]);
+  load_x(min(GG_XD, nk - 1), xr[0]);
   if (threadIdx.x < GG_BM) {
     s_row[threadIdx.x] = meta_row;
     s_rs[threadIdx.x] = meta_rs;
   }
 
-  for (int kt0 = 0; kt0 < nk; kt0 += NW) {
+  // The loop is unrolled by U so that every register set has a fixed name;
+  // all loads are unconditional (steps past the end repeat the last one) and,
+  // without GUARD, the body has no branches.
+  const uint32_t vmask = 0x00780078u, vone = 0x3F803F80u;
+  for (int kt0 = 0; kt0 < nk; kt0 += U) {
 #pragma unroll
-    for (int st = 0; st < NW; ++st) {
+    for (int st = 0; st < U; ++st) {
       const int kt = kt0 + st;
-      // younger than this step's activation loads: per step 4 activation
-      // loads, plus the weight loads of each step (or of each quad's last
-      // step) since; QUAD: 7 steps x 4 + 2 quads x 16
-      gg_wait_vmcnt<QUAD ? 7 * 4 + 2 * 16 : 4 * WV + (NW - 1) * (4 + 4 * WV)>();
+      // stage kt & 1 is complete, and every wave is done with stage
+      // (kt + 1) & 1, which step kt - 1 computed on
       gg_barrier();
-      const uint32_t xb_lds = lds_base + (kt % NB) * GG_XSTAGE;
-      // pin this stage's weights here: without it the compiler hoists the
+      store_x((kt + 1) & 1, xr[(st + 1) % GG_XD]);
+      load_x(min(kt + 1 + GG_XD, nk - 1), xr[(st + 1) % GG_XD]);
+      const uint32_t xb_lds = lds_base + (kt & 1) * GG_XSTAGE;
+      // pin this step's weights here: without it the compiler hoists the
       // conversions of all stages to the top of the group, waiting there for
       // every load in flight
-      const int wsl = QUAD ? (st >> 2) : st;   // weight stage of this step
+      const int wsl = QUAD ? ((st >> 2) % NWB) : (st % NW);   // weight stage of this step
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
@@ -346,7 +348,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
             if constexpr (I4) {
               const u32x4g wq = wbuf[wsl][ns][QUAD ? (st & 3) : 0];
               const uint32_t w = d == 0 ? wq.x : d == 1 ? wq.y : d == 2 ? wq.z : wq.w;
-              bv = as_bf16x8(i4_to_bf16(w));
+              bv = as_bf16x8(i4_to_bf16(w, vmask, vone));
             } else {
               bv = as_bf16x8(wbuf[wsl][ns][d]);
             }
@@ -356,10 +358,8 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
           }
         }
       }
-      // refills: the activation stage of step kt + NW goes to the buffer
-      // read at step kt - 1 (free since this step's opening barrier)
-      load_x(min(kt + NW, nk - 1), (kt + NW) % NB);
-      if (!QUAD) load_w(min(kt + NW, nk - 1), wbuf[st]);
+      // weight refill: step kt + NW (its quad) into the registers consumed
+      if (!QUAD) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
       else if ((st & 3) == 3) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
     }
   }
@@ -367,8 +367,6 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // epilogue: lane holds rows m = 16 ms + 4 kg + j of column (weight row) ln
   // of each N-subtile.  gate/up of int4 experts writes h in the order their
   // down projection reads it (nibble pairs (j, j + 4) within groups of 8).
-  gg_wait_vmcnt<0>();
-  gg_barrier();
   const float mul = I4 ? GG_DIV : 1.0f;
 #pragma unroll
   for (int ms = 0; ms < 4; ++ms) {
@@ -397,12 +395,11 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   }
 }
 
-// K steps in flight: eight for int4 weights loaded by quads (64 registers per
-// quad), two for int4 K counts that are not a multiple of 4 and for bf16 (64
-// registers per step); the block runs one wave per SIMD, so the registers
-// and most of the LDS (nine activation stages) are its own.
+// K steps of weights in flight: eight for int4 weights loaded by quads (64
+// registers per quad), two for int4 K counts that are not a multiple of 4 and
+// for bf16 (64 registers per step); the block runs one wave per SIMD, so the
+// registers are its own.
 constexpr int GG_NW_I4 = 8, GG_NW_BF16 = 2;
-constexpr int GG_NB_MAX = GG_NW_I4 + 1;
 
 template <int WDT, bool DOWN>
 __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgTile& t, uint8_t* lds) {
@@ -414,17 +411,16 @@ __device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgTile& t, ui
       else gg_run<WDT, DOWN, 8, true, true>(a, t, lds);
       return;
     }
-    if (nk % 2 == 0) gg_run<WDT, DOWN, 2, false, false>(a, t, lds);
-    else gg_run<WDT, DOWN, 2, true, false>(a, t, lds);
+    gg_run<WDT, DOWN, 2, true, false>(a, t, lds);   // nk is not a multiple of 4 here
   } else {
-    if (nk % GG_NW_BF16 == 0) gg_run<WDT, DOWN, GG_NW_BF16, false, false>(a, t, lds);
+    if (nk % 4 == 0) gg_run<WDT, DOWN, GG_NW_BF16, false, false>(a, t, lds);
     else gg_run<WDT, DOWN, GG_NW_BF16, true, false>(a, t, lds);
   }
 }
 
 template <int WR, int WS, bool DOWN>
 __global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ggemm(GgArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_NB_MAX * GG_XSTAGE + 2 * GG_BM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GG_XSTAGE + 2 * GG_BM * 4];
   GgTile t;
   if (!gg_tile(a, t)) return;
   if (t.shared)
