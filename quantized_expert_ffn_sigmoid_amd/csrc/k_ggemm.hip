@@ -132,21 +132,6 @@ __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
 constexpr int GG_XSTAGE = GG_BM * GG_BK * 2;   // 16 KB
 constexpr int GG_XD = 4;                       // activation register sets in flight
 
-// Four 16-byte LDS reads (the A operands of one K slice), completed inside
-// the statement, so that the compiler places no wait of its own for them.
-__device__ __forceinline__ void gg_lds_read4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
-                                             u32x4g& r0, u32x4g& r1, u32x4g& r2, u32x4g& r3) {
-  asm volatile(
-      "ds_read_b128 %0, %4\n\t"
-      "ds_read_b128 %1, %5\n\t"
-      "ds_read_b128 %2, %6\n\t"
-      "ds_read_b128 %3, %7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
-}
-
 // Workgroup barrier after this wave's LDS writes have completed, without the
 // release fence of __syncthreads (which would also wait for every global load
 // in flight).  The memory clobber keeps LDS accesses on their side of it.
@@ -249,8 +234,6 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
     xsrc[i] = reinterpret_cast<const uint8_t*>(row) +
               (QUAD ? (xc >> 2) * 256 + (xc & 3) * 16 : 16 * xc);
   }
-  const uint32_t lds_base =
-      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)lds);
   const int nk = K / GG_BK;
   auto load_x = [&](int kt, u32x4g (&v)[4]) {
     const int64_t off = QUAD ? (int64_t)(kt >> 2) * 1024 + (kt & 3) * 64 : (int64_t)kt * (GG_BK * 2);
@@ -317,7 +300,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       gg_barrier();
       store_x((kt + 1) & 1, xr[(st + 1) % GG_XD]);
       load_x(min(kt + 1 + GG_XD, nk - 1), xr[(st + 1) % GG_XD]);
-      const uint32_t xb_lds = lds_base + (kt & 1) * GG_XSTAGE;
+      const uint8_t* xs = lds + (kt & 1) * GG_XSTAGE;
       // pin this step's weights here: without it the compiler hoists the
       // conversions of all stages to the top of the group, waiting there for
       // every load in flight
@@ -332,16 +315,10 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
           bf16x8 av[4];
-          {
-            const uint32_t base = xb_lds + ln * (GG_BK * 2) + 16 * ((kg * 4 + d) ^ ln);
-            u32x4g r0, r1, r2, r3;
-            gg_lds_read4(base, base + 16 * GG_BK * 2, base + 32 * GG_BK * 2, base + 48 * GG_BK * 2,
-                         r0, r1, r2, r3);
-            av[0] = as_bf16x8(r0);
-            av[1] = as_bf16x8(r1);
-            av[2] = as_bf16x8(r2);
-            av[3] = as_bf16x8(r3);
-          }
+#pragma unroll
+          for (int ms = 0; ms < 4; ++ms)
+            av[ms] = as_bf16x8(*reinterpret_cast<const u32x4g*>(
+                xs + (16 * ms + ln) * (GG_BK * 2) + 16 * ((kg * 4 + d) ^ ln)));
 #pragma unroll
           for (int ns = 0; ns < 4; ++ns) {
             bf16x8 bv;
