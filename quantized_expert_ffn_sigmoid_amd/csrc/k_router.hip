@@ -207,8 +207,12 @@ __global__ __launch_bounds__(256) void k_select(SelectParams p, const double* __
                                                 float* __restrict__ topk_w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_token<EPL>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
-                    topk_w + (int64_t)t * p.K, nullptr);
+  if (p.softmax)
+    select_token<EPL, true>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                            topk_w + (int64_t)t * p.K, nullptr);
+  else
+    select_token<EPL, false>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                             topk_w + (int64_t)t * p.K, nullptr);
 }
 
 // Decode: selection of all T <= 16 tokens (one wave each) and the grouping,
@@ -221,9 +225,14 @@ __global__ __launch_bounds__(256) void k_select_bucket(
     int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
   __shared__ int32_t s_idx[kDecodeTokens * kMaxTopK];
   const int nw = blockDim.x >> 6;
-  for (int t = threadIdx.x >> 6; t < T; t += nw)
-    select_token<EPL>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
-                      topk_w + (int64_t)t * p.K, s_idx + t * p.K);
+  for (int t = threadIdx.x >> 6; t < T; t += nw) {
+    if (p.softmax)
+      select_token<EPL, true>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                              topk_w + (int64_t)t * p.K, s_idx + t * p.K);
+    else
+      select_token<EPL, false>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                               topk_w + (int64_t)t * p.K, s_idx + t * p.K);
+  }
   __syncthreads();
   bucket_small(T, p.K, p.E, s_idx, counts, offsets, entries, inverse, active, n_active);
 }

@@ -46,34 +46,37 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// One all-reduce step of (value, index) best-of with the partner of a move.
+// One all-reduce step of (value, index) best-of with the partner of a move
+// (selects, no branches).
 template <int CTRL>
 __device__ __forceinline__ void argbest_step_dpp(double& v, int& i) {
   const double ov = dpp_d<CTRL>(v);
   const int oi = dpp_i<CTRL>(i);
-  if (beats(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
+  const bool take = beats(ov, oi, v, i);
+  v = take ? ov : v;
+  i = take ? oi : i;
 }
 
-__device__ __forceinline__ void argbest_step_xor(double& v, int& i, int m) {
-  const double ov = __shfl_xor(v, m, kWave);
-  const int oi = __shfl_xor(i, m, kWave);
-  if (beats(ov, oi, v, i)) {
-    v = ov;
-    i = oi;
-  }
-}
-
-// Wave-wide best (value, index); every lane receives the winner.
+// Wave-wide best (value, index), returned wave-uniform: every row of 16
+// lanes reduces with register moves, then the four row results are compared
+// through lane reads.
 __device__ __forceinline__ void wave_argbest(double& v, int& i) {
   argbest_step_dpp<kDppXor1>(v, i);
   argbest_step_dpp<kDppXor2>(v, i);
   argbest_step_dpp<kDppHalfMirror>(v, i);
   argbest_step_dpp<kDppMirror>(v, i);
-  argbest_step_xor(v, i, 16);
-  argbest_step_xor(v, i, 32);
+  double bv = readlane_d(v, 0);
+  int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) {
+    const double ov = readlane_d(v, 16 * r);
+    const int oi = __builtin_amdgcn_readlane(i, 16 * r);
+    const bool take = beats(ov, oi, bv, bi);
+    bv = take ? ov : bv;
+    bi = take ? oi : bi;
+  }
+  v = bv;
+  i = bi;
 }
 
 // Two largest values (a >= b) merged with a partner's pair.
@@ -110,48 +113,45 @@ struct SelectParams {
 // k expert indices and weights (rank order) to idx_out / w_out, and the
 // indices also to idx_lds when given.  Lane l holds experts l*EPL ..
 // l*EPL+EPL-1, so a group is a run of consecutive lanes when EPL divides the
-// group size.
-template <int EPL>
+// group size.  Closed (or absent) experts carry -inf; the candidate loops use
+// selects, and the loops over groups and ranks are wave-uniform.
+template <int EPL, bool SOFTMAX>
 __device__ __forceinline__ void select_token(const SelectParams& p, const double* __restrict__ zt,
                                              const float* __restrict__ bias, int32_t* idx_out,
                                              float* w_out, int32_t* idx_lds) {
   const int lane = threadIdx.x & 63;
   const double NEG = -INFINITY;
   double c[EPL], sv[EPL];
-  bool open[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane * EPL + i;
     const bool ok = e < p.E;
-    const double zv = ok ? zt[e] : 0.0;
-    if (p.softmax) {
+    const int ec = ok ? e : p.E - 1;
+    const double zv = zt[ec];
+    if constexpr (SOFTMAX) {
       sv[i] = zv;
       c[i] = ok ? zv : NEG;
     } else {
       const double s = 1.0 / (1.0 + exp(-zv));
       sv[i] = s;
-      c[i] = ok ? s + (bias ? (double)bias[e] : 0.0) : NEG;
+      const double bb = bias ? (double)bias[ec] : 0.0;
+      c[i] = ok ? s + bb : NEG;
     }
-    open[i] = ok;
   }
 
-  if (!p.softmax && p.topk_group < p.G) {
+  if (!SOFTMAX && p.topk_group < p.G) {
     const int per = p.E / p.G;
     const int lpg = per / EPL;
     const bool seg = per % EPL == 0 && lpg >= 1 && lpg <= kWave && (lpg & (lpg - 1)) == 0;
     if (seg) {
       // every lane's experts lie in one group: segmented top-2, then rank the
-      // groups against each other through scalar broadcasts
+      // groups against each other through lane reads
       double a = NEG, b = NEG;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        if (!open[i]) continue;
-        if (c[i] > a) {
-          b = a;
-          a = c[i];
-        } else if (c[i] > b) {
-          b = c[i];
-        }
+        const double hi = fmax(a, c[i]), lo = fmin(a, c[i]);
+        b = fmax(b, lo);
+        a = hi;
       }
       segment_top2(a, b, lpg);
       const double gs = per == 1 ? a : a + b;
@@ -163,7 +163,7 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
       }
       if (rank >= p.topk_group) {
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) open[i] = false;
+        for (int i = 0; i < EPL; ++i) c[i] = NEG;
       }
     } else {
       // general shapes: one group at a time
@@ -173,14 +173,10 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
           const int e = lane * EPL + i;
-          if (open[i] && e / per == g) {
-            if (c[i] > a) {
-              b = a;
-              a = c[i];
-            } else if (c[i] > b) {
-              b = c[i];
-            }
-          }
+          const double x = e / per == g ? c[i] : NEG;
+          const double hi = fmax(a, x), lo = fmin(a, x);
+          b = fmax(b, lo);
+          a = hi;
         }
         wave_top2(a, b);
         if (lane == g) my_gs = (per == 1) ? a : a + b;
@@ -196,7 +192,7 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = lane * EPL + i;
-        if (open[i] && !((kept >> (e / per)) & 1ull)) open[i] = false;
+        if (!((kept >> (e / per)) & 1ull)) c[i] = NEG;
       }
     }
   }
@@ -205,17 +201,16 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
   int my_idx = 0;
   double my_s = 0.0, ssum = 0.0, z0 = 0.0;
   for (int j = 0; j < p.K; ++j) {
-    double v = NEG;
+    // the lane's best: ascending experts, so a strictly larger value wins
+    // and equal values keep the lower index
+    double v = NEG, bs = 0.0;
     int bi = 0x7FFFFFFF;
-    double bs = 0.0;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const int e = lane * EPL + i;
-      if (open[i] && beats(c[i], e, v, bi)) {
-        v = c[i];
-        bi = e;
-        bs = sv[i];
-      }
+      const bool take = c[i] > v;
+      v = take ? c[i] : v;
+      bi = take ? lane * EPL + i : bi;
+      bs = take ? sv[i] : bs;
     }
     double rv = v;
     int ri = bi;
@@ -223,20 +218,17 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     const int owner = min(ri / EPL, kWave - 1);
     const double s_win = readlane_d(bs, owner);
 #pragma unroll
-    for (int i = 0; i < EPL; ++i)
-      if (lane * EPL + i == ri) open[i] = false;
+    for (int i = 0; i < EPL; ++i) c[i] = lane * EPL + i == ri ? NEG : c[i];
     double contrib;
-    if (p.softmax) {
+    if constexpr (SOFTMAX) {
       if (j == 0) z0 = s_win;
       contrib = exp(s_win - z0);
     } else {
       contrib = s_win;
     }
     ssum += contrib;   // sequential sum in rank order
-    if (lane == j) {
-      my_idx = ri;
-      my_s = contrib;
-    }
+    my_idx = lane == j ? ri : my_idx;
+    my_s = lane == j ? contrib : my_s;
   }
   if (lane < p.K) {
     idx_out[lane] = my_idx;
@@ -257,50 +249,58 @@ constexpr int BK_SMALL = 512;     // slot counts up to this take the direct path
 
 // Small slot counts (F <= BK_SMALL): a slot's position is (slots of smaller
 // experts) + (earlier slots of the same expert); every expert counts its
-// slots itself.  Any block size.
+// slots itself, scanning the slot keys four at a time.  Any block size.
 __device__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx,
                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                              int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
                              int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
-  __shared__ int s_key[BK_SMALL];
+  // s_key: expert of the slot or -1 (invalid index, or padding to a multiple
+  // of 4); s_kf: 2 * key + (first slot of its expert), or -1
+  __shared__ __attribute__((aligned(16))) int s_key[BK_SMALL];
+  __shared__ __attribute__((aligned(16))) int s_kf[BK_SMALL];
   __shared__ int s_rank[BK_SMALL];
   __shared__ int s_off[kMaxExperts];
   const int tid = threadIdx.x, nth = blockDim.x;
-  const int F = T * K;
-  for (int f = tid; f < F; f += nth) {
-    const int e = idx[f];
+  const int F = T * K, F4 = (F + 3) & ~3;
+  for (int f = tid; f < F4; f += nth) {
+    const int e = f < F ? idx[f] : -1;
     s_key[f] = (e >= 0 && e < E) ? e : -1;
   }
   __syncthreads();
-  for (int f = tid; f < F; f += nth) {
+  for (int f = tid; f < F4; f += nth) {
     const int key = s_key[f];
     int r = 0;
-    for (int g = 0; g < f; ++g) r += s_key[g] == key ? 1 : 0;
+    for (int g = 0; g < f; g += 4) {
+      const int4 k4 = *reinterpret_cast<const int4*>(s_key + g);
+      r += (k4.x == key) + (g + 1 < f && k4.y == key) + (g + 2 < f && k4.z == key) +
+           (g + 3 < f && k4.w == key);
+    }
     s_rank[f] = r;
+    s_kf[f] = key < 0 ? -1 : 2 * key + (r == 0 ? 1 : 0);
   }
   __syncthreads();
   for (int e = tid; e < E; e += nth) {
     int off = 0, cnt = 0, before = 0;
-    for (int f = 0; f < F; ++f) {
-      const int key = s_key[f];
-      if (key < 0) continue;
-      off += key < e ? 1 : 0;
-      cnt += key == e ? 1 : 0;
-      before += (key < e && s_rank[f] == 0) ? 1 : 0;
+#pragma unroll 4
+    for (int g = 0; g < F4; g += 4) {
+      const int4 v = *reinterpret_cast<const int4*>(s_kf + g);
+      const int kf[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool lt = kf[q] >= 0 && kf[q] < 2 * e;
+        off += lt ? 1 : 0;
+        cnt += (kf[q] >> 1) == e ? 1 : 0;
+        before += (lt && (kf[q] & 1)) ? 1 : 0;
+      }
     }
     counts[e] = cnt;
     offsets[e] = off;
     s_off[e] = off;
     if (cnt) active[before] = e;
-  }
-  if (tid == 0) {
-    int tot = 0, distinct = 0;
-    for (int f = 0; f < F; ++f) {
-      tot += s_key[f] >= 0 ? 1 : 0;
-      distinct += (s_key[f] >= 0 && s_rank[f] == 0) ? 1 : 0;
+    if (e == E - 1) {
+      offsets[E] = off + cnt;
+      n_active[0] = before + (cnt ? 1 : 0);
     }
-    offsets[E] = tot;
-    n_active[0] = distinct;
   }
   __syncthreads();
   for (int f = tid; f < F; f += nth) {
