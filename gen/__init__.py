@@ -31,12 +31,12 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 # dtype codes (match the enum values used at both library boundaries)
-F32, BF16, I4, I2 = 0, 1, 2, 3
+F32, BF16, I4, I2, I8 = 0, 1, 2, 3, 4
 SIGMOID_NOAUX_TC, SOFTMAX_TOPK = 0, 1
 
 # tensor ids of gen_core.h
 T_X, T_WROUTER, T_BIAS, T_GU_CODES, T_GU_SCALES, T_DN_CODES, T_DN_SCALES = 0, 1, 2, 3, 4, 5, 6
-T_GU_BF16, T_DN_BF16, T_ZIPF_PERM = 7, 8, 9
+T_GU_BF16, T_DN_BF16, T_ZIPF_PERM, T_GU_I8, T_DN_I8 = 7, 8, 9, 10, 11
 
 SCALE_LO, SCALE_WIDTH = 0.01, 0.04   # per-row scales U(0.01, 0.05)
 
@@ -129,6 +129,8 @@ def row_bytes(dtype: int, cols: int) -> int:
         return cols // 2
     if dtype == I2:
         return cols // 4
+    if dtype == I8:
+        return cols
     if dtype == BF16:
         return cols * 2
     if dtype == F32:
@@ -168,8 +170,10 @@ def host_lib():
         lib.gen_fill_normal_bf16.argtypes = [vp, i64, u64, i32, i32, i32, dbl]
         lib.gen_fill_u64.argtypes = [vp, i64, u64, i32, i32, i32]
         lib.gen_int2_from_int4.argtypes = [vp, vp, i64, i64, vp, vp]
+        lib.gen_fill_int8.argtypes = [vp, u64, i32, i32, i32, i64]
         for fn in (lib.gen_fill_int4, lib.gen_fill_scales, lib.gen_fill_normal_f32,
-                   lib.gen_fill_normal_bf16, lib.gen_fill_u64, lib.gen_int2_from_int4):
+                   lib.gen_fill_normal_bf16, lib.gen_fill_u64, lib.gen_int2_from_int4,
+                   lib.gen_fill_int8):
             fn.restype = None
         _host = lib
     return _host
@@ -184,6 +188,36 @@ def int4_codes(seed, layer, tensor, expert, rows, cols) -> np.ndarray:
     out = np.empty((rows, cols // 2), dtype=np.uint8)
     host_lib().gen_fill_int4(_p(out), seed, layer, tensor, expert, out.size)
     return out
+
+
+def int8_codes(seed, layer, tensor, expert, rows, cols) -> np.ndarray:
+    """int8 codes uniform on {-127..127}, row-major [rows][cols] bytes."""
+    out = np.empty((rows, cols), dtype=np.uint8)
+    host_lib().gen_fill_int8(_p(out), seed, layer, tensor, expert, out.size)
+    return out
+
+
+def int8_from_int4(codes4: np.ndarray, cols: int) -> np.ndarray:
+    """The int8 container holding the same codes as a packed int4 matrix
+    (each nibble sign-extended to a byte)."""
+    b = np.ascontiguousarray(codes4, dtype=np.uint8).reshape(-1, cols // 2)
+    lo = (b & 0xF).astype(np.int16)
+    hi = (b >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty((b.shape[0], cols), dtype=np.int16)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out.astype(np.int8).view(np.uint8)
+
+
+def expert_i8_from_i4(ex: dict, hidden: int, inter: int) -> dict:
+    """An int4 expert re-packed into the int8 container (same codes, same
+    scales)."""
+    assert ex["dtype"] == I4
+    return dict(dtype=I8, gate_up=int8_from_int4(ex["gate_up"], hidden),
+                gate_up_scale=ex["gate_up_scale"], down=int8_from_int4(ex["down"], inter),
+                down_scale=ex["down_scale"])
 
 
 def scales(seed, layer, tensor, expert, rows, mult) -> np.ndarray:
@@ -290,13 +324,21 @@ def expert(cfg: Config, layer: int, e: int, dtype: Optional[int] = None, shared:
     """Host copy of one expert: dict(gate_up, gate_up_scale, down, down_scale).
 
     Routed experts use expert index e; the shared expert uses index n_experts
-    (its own streams).  int2 experts are derived from the int4 ones.
+    (its own streams).  int2 experts are derived from the int4 ones; int8
+    experts draw full-range codes from their own streams, with the int4 scale
+    streams divided by 16 (weights of similar magnitude).
     """
     H = cfg.hidden
     I = cfg.inter * (cfg.n_shared if shared else 1)
     if dtype is None:
         dtype = cfg.shared_dtype if shared else cfg.expert_dtype
     eid = cfg.n_experts if shared else e
+    if dtype == I8:
+        gu = int8_codes(cfg.seed, layer, T_GU_I8, eid, 2 * I, H)
+        gus = scales(cfg.seed, layer, T_GU_SCALES, eid, 2 * I, scale_mult(cfg, H) / 16.0)
+        dn = int8_codes(cfg.seed, layer, T_DN_I8, eid, H, I)
+        dns = scales(cfg.seed, layer, T_DN_SCALES, eid, H, scale_mult(cfg, I) / 16.0)
+        return dict(dtype=I8, gate_up=gu, gate_up_scale=gus, down=dn, down_scale=dns)
     if dtype == BF16:
         gu = normal_bf16((2 * I, H), cfg.seed, layer, T_GU_BF16, eid, cfg.bf16_std)
         dn = normal_bf16((H, I), cfg.seed, layer, T_DN_BF16, eid, cfg.bf16_std)

@@ -18,8 +18,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (BF16, I2, I4, SCALE_LO, SCALE_WIDTH, T_DN_CODES, T_DN_SCALES, T_GU_CODES,
-               T_GU_SCALES, Config, HostLayer, expert, expert_bytes, router, scale_mult)
+from . import (BF16, I2, I4, I8, SCALE_LO, SCALE_WIDTH, T_DN_CODES, T_DN_I8, T_DN_SCALES,
+               T_GU_CODES, T_GU_I8, T_GU_SCALES, Config, HostLayer, expert, expert_bytes, router,
+               scale_mult)
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 _dev = None
@@ -39,8 +40,9 @@ def dev_lib():
                                               dbl, vp]
         L.gen_dev_int2_from_int4_set.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, i32, i64,
                                                  i64, vp]
+        L.gen_dev_fill_int8_set.argtypes = [vp, i64, i32, i64, u64, i32, i32, i32, vp]
         for f in (L.gen_dev_fill_int4_set, L.gen_dev_fill_scales_set,
-                  L.gen_dev_int2_from_int4_set):
+                  L.gen_dev_int2_from_int4_set, L.gen_dev_fill_int8_set):
             f.restype = ctypes.c_int
         _dev = L
     return _dev
@@ -181,6 +183,22 @@ def generate_device_layer(cfg: Config, layer: int, device, dtype: Optional[int] 
         lay = blob_layout(BF16, H, I)
         blobs = np.stack([_host_blob(expert(cfg, layer, e, BF16), lay) for e in range(E)])
         return DeviceLayer(cfg, BF16, w_t, b_t, _upload(blobs, device), lay, sh, sh_lay)
+    if dtype == I8:
+        lay = blob_layout(I8, H, I)
+        t8 = torch.empty((E, lay["stride"]), dtype=torch.uint8, device=device)
+        L = dev_lib()
+        base = t8.data_ptr()
+        _check(L.gen_dev_fill_int8_set(base + lay["gate_up"], lay["stride"], E, 2 * I * H,
+                                       cfg.seed, layer, T_GU_I8, 0, stream), "int8 gate/up codes")
+        _check(L.gen_dev_fill_int8_set(base + lay["down"], lay["stride"], E, H * I, cfg.seed,
+                                       layer, T_DN_I8, 0, stream), "int8 down codes")
+        _check(L.gen_dev_fill_scales_set(base + lay["gate_up_scale"], lay["stride"], E, 2 * I,
+                                         cfg.seed, layer, T_GU_SCALES, 0, SCALE_LO, SCALE_WIDTH,
+                                         scale_mult(cfg, H) / 16.0, stream), "gate/up scales")
+        _check(L.gen_dev_fill_scales_set(base + lay["down_scale"], lay["stride"], E, H, cfg.seed,
+                                         layer, T_DN_SCALES, 0, SCALE_LO, SCALE_WIDTH,
+                                         scale_mult(cfg, I) / 16.0, stream), "down scales")
+        return DeviceLayer(cfg, I8, w_t, b_t, t8, lay, sh, sh_lay)
     lay4 = blob_layout(I4, H, I)
     t4 = torch.empty((E, lay4["stride"]), dtype=torch.uint8, device=device)
     _fill_int4_blobs(cfg, layer, t4, lay4, stream)

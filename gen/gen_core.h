@@ -37,7 +37,9 @@ enum {
   GEN_T_DN_SCALES = 6,  /* down per-row scales [H]                      */
   GEN_T_GU_BF16 = 7,    /* gate/up bf16 weights [2I][H]                 */
   GEN_T_DN_BF16 = 8,    /* down bf16 weights [H][I]                     */
-  GEN_T_ZIPF_PERM = 9   /* expert popularity permutation                */
+  GEN_T_ZIPF_PERM = 9,  /* expert popularity permutation                */
+  GEN_T_GU_I8 = 10,     /* gate/up int8 codes [2I][H]                   */
+  GEN_T_DN_I8 = 11      /* down int8 codes [H][I]                       */
 };
 
 GEN_FN uint64_t gen_mix64(uint64_t z) {
@@ -76,6 +78,15 @@ GEN_FN uint8_t gen_int4_byte(uint64_t key, uint64_t byte_index) {
   int lo = (int)gen_below((uint32_t)(r & 0xFFFFFFFFu), 15u) - 7;
   int hi = (int)gen_below((uint32_t)(r >> 32), 15u) - 7;
   return (uint8_t)(((unsigned)lo & 0xFu) | (((unsigned)hi & 0xFu) << 4));
+}
+
+/* Two int8 codes, each uniform on {-127, ..., 127}: element 2i in the low
+ * byte, element 2i+1 in the high byte, two's complement. */
+GEN_FN uint16_t gen_int8_pair(uint64_t key, uint64_t pair_index) {
+  uint64_t r = gen_draw(key, pair_index);
+  int lo = (int)gen_below((uint32_t)(r & 0xFFFFFFFFu), 255u) - 127;
+  int hi = (int)gen_below((uint32_t)(r >> 32), 255u) - 127;
+  return (uint16_t)(((unsigned)lo & 0xFFu) | (((unsigned)hi & 0xFFu) << 8));
 }
 
 /* Signed value of nibble j (0 or 1) of a packed int4 byte. */

@@ -33,6 +33,26 @@ __global__ void k_fill_int4_set(uint8_t* dst, int64_t stride, int64_t bytes_per_
       out[i] = gen_int4_byte(key, (uint64_t)i);
 }
 
+__global__ void k_fill_int8_set(uint8_t* dst, int64_t stride, int64_t bytes_per_expert,
+                                uint64_t seed, int32_t layer, int32_t tensor, int32_t expert0) {
+  const int e = blockIdx.y;
+  const uint64_t key = gen_key(seed, (uint64_t)layer, (uint64_t)tensor, (uint64_t)(expert0 + e));
+  uint8_t* out = dst + (int64_t)e * stride;
+  /* 4 bytes (two pairs) per thread per step: one 32-bit store */
+  const int64_t n4 = bytes_per_expert / 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t w = (uint32_t)gen_int8_pair(key, (uint64_t)(2 * i)) |
+                       ((uint32_t)gen_int8_pair(key, (uint64_t)(2 * i + 1)) << 16);
+    reinterpret_cast<uint32_t*>(out)[i] = w;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0 && (bytes_per_expert & 3)) {
+    const uint16_t v = gen_int8_pair(key, (uint64_t)(2 * n4));
+    out[4 * n4] = (uint8_t)(v & 0xFFu);
+    out[4 * n4 + 1] = (uint8_t)(v >> 8);
+  }
+}
+
 __global__ void k_fill_scales_set(uint8_t* dst, int64_t stride, int64_t rows, uint64_t seed,
                                   int32_t layer, int32_t tensor, int32_t expert0, double lo,
                                   double width, double mult) {
@@ -102,6 +122,19 @@ int gen_dev_fill_int4_set(void* dst, int64_t stride, int32_t n_experts, int64_t 
   if (n_experts <= 0 || bytes_per_expert <= 0) return 0;
   dim3 grid(grid_for(bytes_per_expert / 4, 256 * 4), n_experts);
   hipLaunchKernelGGL(k_fill_int4_set, grid, dim3(256), 0, s, (uint8_t*)dst, stride,
+                     bytes_per_expert, seed, layer, tensor, expert0);
+  return (int)hipGetLastError();
+}
+
+/* Fill n_experts int8 matrices of bytes_per_expert (even) bytes each, the
+ * e-th at dst + e*stride, with the stream of expert (expert0 + e). */
+int gen_dev_fill_int8_set(void* dst, int64_t stride, int32_t n_experts, int64_t bytes_per_expert,
+                          uint64_t seed, int32_t layer, int32_t tensor, int32_t expert0,
+                          hipStream_t s) {
+  if (bytes_per_expert & 1) return (int)hipErrorInvalidValue;   /* whole pairs only */
+  if (n_experts <= 0 || bytes_per_expert <= 0) return 0;
+  dim3 grid(grid_for(bytes_per_expert / 4, 256 * 4), n_experts);
+  hipLaunchKernelGGL(k_fill_int8_set, grid, dim3(256), 0, s, (uint8_t*)dst, stride,
                      bytes_per_expert, seed, layer, tensor, expert0);
   return (int)hipGetLastError();
 }

@@ -44,6 +44,18 @@ void gen_fill_int4(uint8_t* dst, uint64_t seed, int32_t layer, int32_t tensor, i
   for (int64_t i = 0; i < n_bytes; ++i) dst[i] = gen_int4_byte(key, (uint64_t)i);
 }
 
+/* int8 codes of one matrix of one expert: n_bytes bytes (even). */
+void gen_fill_int8(uint8_t* dst, uint64_t seed, int32_t layer, int32_t tensor, int32_t expert,
+                   int64_t n_bytes) {
+  uint64_t key = gen_key(seed, (uint64_t)layer, (uint64_t)tensor, (uint64_t)expert);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_bytes / 2; ++i) {
+    uint16_t v = gen_int8_pair(key, (uint64_t)i);
+    dst[2 * i] = (uint8_t)(v & 0xFFu);
+    dst[2 * i + 1] = (uint8_t)(v >> 8);
+  }
+}
+
 /* Per-row scales of one matrix of one expert. */
 void gen_fill_scales(float* dst, uint64_t seed, int32_t layer, int32_t tensor, int32_t expert,
                      int64_t rows, double lo, double width, double mult) {

@@ -51,7 +51,13 @@ typedef enum {
   MOE_EHIP = 4           /* a HIP launch or runtime call failed                   */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I4 = 2, MOE_I2 = 3 } moe_dtype;
+/* Weight containers ("colibri" README, "What's implemented": packed int4 and
+ * packed int2 with per-row scales, validated against an int8 container):
+ * MOE_I4: element i of a row in byte i/2, low nibble first, two's complement;
+ * MOE_I2: element i in byte i/4 at bits 2(i%4), two's complement; MOE_I8:
+ * element i is byte i, two's complement.  Integer weights are code * (fp32
+ * row scale).  MOE_BF16: bf16 weights, no scales. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_I4 = 2, MOE_I2 = 3, MOE_I8 = 4 } moe_dtype;
 
 typedef enum { MOE_ROUTER_SIGMOID_NOAUX_TC = 0, MOE_ROUTER_SOFTMAX_TOPK = 1 } moe_router;
 
@@ -65,12 +71,12 @@ typedef struct {
   int32_t n_group;         /* sigmoid router: contiguous expert groups (1 = none)     */
   int32_t topk_group;      /* sigmoid router: groups kept per token                   */
   float routed_scaling;    /* routed_scaling_factor (1.0 for softmax layers)          */
-  int32_t expert_dtype;    /* MOE_I4 | MOE_I2 | MOE_BF16                              */
+  int32_t expert_dtype;    /* MOE_I4 | MOE_I2 | MOE_I8 | MOE_BF16                     */
   int32_t act_dtype;       /* MOE_F32 | MOE_BF16: type of x; with MOE_BF16 the        */
                            /* SwiGLU output h is rounded to bf16 before the down     */
                            /* projection                                             */
   int32_t n_shared;        /* 0 or 1 shared expert (intermediate size n_shared * I)   */
-  int32_t shared_dtype;    /* MOE_I4 | MOE_I2 | MOE_BF16                              */
+  int32_t shared_dtype;    /* MOE_I4 | MOE_I2 | MOE_I8 | MOE_BF16                     */
   float norm_eps;          /* RMSNorm epsilon used by moe_stack_forward               */
 } moe_layer_desc;
 

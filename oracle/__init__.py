@@ -18,7 +18,7 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-BF16, I4, I2 = 1, 2, 3
+BF16, I4, I2, I8 = 1, 2, 3, 4
 SIGMOID_NOAUX_TC, SOFTMAX_TOPK = 0, 1
 
 

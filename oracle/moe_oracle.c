@@ -24,7 +24,7 @@
  *     round to nearest, ties to even (our rule for every narrowing cast).
  *
  * Arithmetic: every input widens exactly to double.  A code times its
- * float scale is exact in double (at most 4 + 24 significant bits), and that
+ * float scale is exact in double (at most 8 + 24 significant bits), and that
  * times a float activation is exact too (at most 52 bits); sums run in index
  * order in double.  The only roundings to narrower types are the ones the
  * layer defines: topk weights to float, h to bf16 when activations are bf16,
@@ -88,20 +88,29 @@ static double x_at(const void* x, int bf16, int64_t i) {
 
 /* Packed int4: element i sits in byte i/2, low nibble first (even elements in
  * bits 0-3), as a two's-complement nibble.  Packed int2: element i sits in byte
- * i/4 at bits 2*(i%4)..2*(i%4)+1, two's complement.  ("colibri" README, "What's
- * implemented": packed int4 / packed int2 containers.) */
+ * i/4 at bits 2*(i%4)..2*(i%4)+1, two's complement.  int8: element i is byte i,
+ * two's complement.  ("colibri" README, "What's implemented": packed int4 /
+ * packed int2 containers next to the int8 container they were validated
+ * against.) */
 static int code_at(int32_t dtype, const uint8_t* p, int64_t i) {
   if (dtype == ORC_I4) {
     int v = (p[i / 2] >> (4 * (int)(i % 2))) & 0xF;
     return v >= 8 ? v - 16 : v;
-  } else {
+  } else if (dtype == ORC_I2) {
     int v = (p[i / 4] >> (2 * (int)(i % 4))) & 0x3;
     return v >= 2 ? v - 4 : v;
+  } else {
+    int v = p[i];
+    return v >= 128 ? v - 256 : v;
   }
 }
 
+static int is_code_dtype(int32_t dtype) {
+  return dtype == ORC_I4 || dtype == ORC_I2 || dtype == ORC_I8;
+}
+
 int orc_decode_codes(int32_t dtype, const uint8_t* packed, int64_t n, int8_t* out) {
-  if (dtype != ORC_I4 && dtype != ORC_I2) return ORC_EINVAL;
+  if (!is_code_dtype(dtype)) return ORC_EINVAL;
   for (int64_t i = 0; i < n; ++i) out[i] = (int8_t)code_at(dtype, packed, i);
   return ORC_OK;
 }
@@ -109,6 +118,7 @@ int orc_decode_codes(int32_t dtype, const uint8_t* packed, int64_t n, int8_t* ou
 static int64_t row_bytes(int32_t dtype, int64_t cols) {
   if (dtype == ORC_I4) return cols / 2;
   if (dtype == ORC_I2) return cols / 4;
+  if (dtype == ORC_I8) return cols;
   return cols * 2;
 }
 
@@ -125,7 +135,7 @@ static double weight_at(int32_t dtype, const void* m, const float* scale, int64_
  * scale, round to nearest even. */
 int orc_dequant_rows(int32_t dtype, const void* codes, const float* scales, int64_t cols,
                      int64_t row0, int64_t n_rows, float* out) {
-  if (dtype != ORC_I4 && dtype != ORC_I2 && dtype != ORC_BF16) return ORC_EINVAL;
+  if (!is_code_dtype(dtype) && dtype != ORC_BF16) return ORC_EINVAL;
   for (int64_t r = 0; r < n_rows; ++r) {
     for (int64_t c = 0; c < cols; ++c) {
       if (dtype == ORC_BF16) {

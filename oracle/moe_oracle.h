@@ -14,7 +14,7 @@
 
 #include <stdint.h>
 
-enum { ORC_BF16 = 1, ORC_I4 = 2, ORC_I2 = 3 };
+enum { ORC_BF16 = 1, ORC_I4 = 2, ORC_I2 = 3, ORC_I8 = 4 };
 enum { ORC_ROUTER_SIGMOID_NOAUX_TC = 0, ORC_ROUTER_SOFTMAX_TOPK = 1 };
 enum { ORC_OK = 0, ORC_EINVAL = 1, ORC_EMISSING = 2 };
 
@@ -23,10 +23,10 @@ typedef struct {
   int32_t router;             /* ORC_ROUTER_*                                   */
   int32_t n_group, topk_group;
   double routed_scaling;
-  int32_t expert_dtype;       /* ORC_BF16 | ORC_I4 | ORC_I2                     */
+  int32_t expert_dtype;       /* ORC_BF16 | ORC_I4 | ORC_I2 | ORC_I8            */
   int32_t act_bf16;           /* 1: x is bf16 and h is rounded to bf16          */
   int32_t n_shared;           /* 0 or 1                                         */
-  int32_t shared_dtype;       /* ORC_BF16 | ORC_I4 | ORC_I2                     */
+  int32_t shared_dtype;       /* ORC_BF16 | ORC_I4 | ORC_I2 | ORC_I8            */
 } orc_desc;
 
 /* One expert set.  Each table has one entry per expert; an entry may be NULL

@@ -45,6 +45,14 @@ struct Fmt<MOE_I2> {
   static constexpr int EPG = 32, GB = 8, DW = 2;
   static constexpr float OFF = 2.0f, UNIT = 1.0f / 512.0f;
 };
+// int8: 32 codes in two 16-byte halves; a code q is read as the float
+// (q + OFF) * UNIT, the same operand the int4 format yields for q in
+// [-8, 7], so that int4 codes widened to int8 give bit-identical results.
+template <>
+struct Fmt<MOE_I8> {
+  static constexpr int EPG = 32, GB = 32, DW = 8;
+  static constexpr float OFF = 8.0f, UNIT = 1.0f / 512.0f;
+};
 template <>
 struct Fmt<MOE_BF16> {
   static constexpr int EPG = 8, GB = 16, DW = 4;
@@ -59,7 +67,18 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // activations and router weights in the caches.
 template <int WDT>
 __device__ __forceinline__ void load_granule(const uint8_t* p, uint32_t (&g)[Fmt<WDT>::DW]) {
-  if constexpr (Fmt<WDT>::DW == 4) {
+  if constexpr (Fmt<WDT>::DW == 8) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 16));
+    g[0] = v.x;
+    g[1] = v.y;
+    g[2] = v.z;
+    g[3] = v.w;
+    g[4] = w.x;
+    g[5] = w.y;
+    g[6] = w.z;
+    g[7] = w.w;
+  } else if constexpr (Fmt<WDT>::DW == 4) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     g[0] = v.x;
     g[1] = v.y;
@@ -69,6 +88,24 @@ __device__ __forceinline__ void load_granule(const uint8_t* p, uint32_t (&g)[Fmt
     const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
     g[0] = v.x;
     g[1] = v.y;
+  }
+}
+
+// 16 int8 codes (four dwords, element order) dotted with x[n][e0 .. e0+15]:
+// offset bytes b = q + 128 are read exactly as floats, and (q + 8) * UNIT is
+// one exact fma -- for q in [-8, 7] the very operand the int4 format yields.
+template <int NT, int KSL>
+__device__ __forceinline__ void i8_half_fma(const uint32_t (&gr)[4], const float (&x)[NT][KSL],
+                                            int e0, float (&acc)[NT]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t w = gr[d] ^ 0x80808080u;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float q = fmaf((float)((w >> (8 * b)) & 0xFFu), 1.0f / 512.0f, -120.0f / 512.0f);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] = fmaf(q, x[n][e0 + 4 * d + b], acc[n]);
+    }
   }
 }
 
@@ -102,6 +139,11 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
         }
       }
     }
+  } else if constexpr (WDT == MOE_I8) {
+    const uint32_t lo[4] = {gr[0], gr[1], gr[2], gr[3]};
+    const uint32_t hi[4] = {gr[4], gr[5], gr[6], gr[7]};
+    i8_half_fma<NT, KSL>(lo, x, b0, acc);
+    i8_half_fma<NT, KSL>(hi, x, b0 + 16, acc);
   } else if constexpr (WDT == MOE_I2) {
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
@@ -203,11 +245,13 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 
 // Pipelining step: CG granules of each of the NM rows of a pass (a row's GPL
-// granules take GPL / CG steps).  CG * NM <= 6 keeps a step at <= 96 bytes
-// per lane; PF steps are in flight while one is computed.
-template <int GPL, int NM>
+// granules take GPL / CG steps).  A step holds at most 96 bytes per lane (six
+// 16-byte or three 32-byte granules; 8-byte granules count as 16); PF steps
+// are in flight while one is computed.
+template <int GPL, int NM, int GB>
 struct StepShape {
-  static constexpr int cg_for(int c) { return (GPL % c == 0 && c * NM <= 6) ? c : cg_for(c - 1); }
+  static constexpr int kMaxG = GB > 16 ? 3 : 6;
+  static constexpr int cg_for(int c) { return (GPL % c == 0 && c * NM <= kMaxG) ? c : cg_for(c - 1); }
   static constexpr int CG = cg_for(GPL < 6 ? GPL : 6);
   static constexpr int STEPS = GPL / CG;
   static constexpr int PF = CG * NM >= 4 ? 2 : (CG * NM >= 2 ? 4 : 8);
@@ -230,7 +274,7 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
   using F = Fmt<WDT>;
   constexpr int EPG = F::EPG, GB = F::GB, DW = F::DW, GPL = KSL / EPG;
   constexpr int NM = PAIR ? 2 : 1;
-  using SS = StepShape<GPL, NM>;
+  using SS = StepShape<GPL, NM, GB>;
   constexpr int CG = SS::CG, STEPS = SS::STEPS, PF = SS::PF;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lpr = jb.lpr, rpp = jb.rpp;
@@ -347,7 +391,8 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
 
 // ------------------------------------------------------------ ring path
 // Rows of at least 64 granules (all 64 lanes of a wave on one row, so every
-// wave load is one contiguous 1 KB run): the codes stream through a per-wave
+// wave load is one contiguous 1 KB run; int8's 32-byte granules take two
+// slots, each a 2 KB run read at every other 16 bytes): the codes stream through a per-wave
 // ring of kRing 1 KB LDS slots filled by direct global-to-LDS loads.  Loads
 // in flight then hold no registers, and a slot is refilled as soon as its
 // data has been consumed, so about kRing KB per wave stay in flight.
@@ -483,8 +528,11 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
                          bool stage_scales, RingLds& L) {
   using F = Fmt<WDT>;
   constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
-  constexpr int NM = PAIR ? 2 : 1, S = NM * GPL;
-  static_assert(GB == 16, "ring slots hold 16-byte granules");
+  constexpr int HPG = GB / 16;   // 16-byte slots per granule: 1, or 2 (int8 halves)
+  constexpr int NM = PAIR ? 2 : 1, S = NM * GPL * HPG;
+  static_assert(GB == 16 || (GB == 32 && WDT == MOE_I8), "ring slots hold 16-byte granules or halves");
+  static_assert(WDT != MOE_I8 || (Fmt<MOE_I8>::UNIT == 1.0f / 512.0f && Fmt<MOE_I8>::OFF == 8.0f),
+                "i8_half_fma's constants");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t rbytes = (int64_t)(jb.K / EPG) * GB;
@@ -496,12 +544,13 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
   const int total = my_rows * S;
   uint8_t* ring = &L.ring[wave][0][0];
   const uint8_t* lane_base = jb.W + (int64_t)jb.r0 * rbytes + lane * GB;
-  // slot n of the stream: local row i = n / S, matrix m, granule g
+  // slot n of the stream: local row i = n / S, matrix m, granule g, half h
   auto issue = [&](int n) {
     const int i = n / S, idx = n - i * S;
-    const int m = idx / GPL, g = idx - m * GPL;
+    const int m = idx / (GPL * HPG), gh = idx - m * (GPL * HPG);
+    const int g = gh / HPG, h = gh - g * HPG;
     const int64_t row = wave + i * kWaves + m * jb.rows;
-    const uint8_t* p = lane_base + row * rbytes + g * (64 * GB);
+    const uint8_t* p = lane_base + row * rbytes + g * (64 * GB) + h * 16;
     __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(ring + (n & (kRing - 1)) * 1024), 16, 0, 0);
   };
   const int pro = total < kRing ? total : kRing;
@@ -545,11 +594,16 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
         vnext = read_slot(sn + 1);
       }
       const uint32_t gr[4] = {v.x, v.y, v.z, v.w};
-      const int mm = idx / GPL, g = idx % GPL;
-      granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
+      const int mm = idx / (GPL * HPG), gh = idx % (GPL * HPG);
+      const int g = gh / HPG, h = gh % HPG;
+      if constexpr (HPG == 1) granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
+      else i8_half_fma<NT, KSL>(gr, x, g * EPG + 16 * h, acc[mm]);
       if constexpr (WDT != MOE_BF16) {
+        // the offset after the granule's last slot
+        if (h == HPG - 1) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) acc[mm][n] = fmaf(-F::OFF * F::UNIT, gs[n][g], acc[mm][n]);
+          for (int n = 0; n < NT; ++n) acc[mm][n] = fmaf(-F::OFF * F::UNIT, gs[n][g], acc[mm][n]);
+        }
       }
       // the slot has been consumed (its data fed the FMAs above): refill it
 #pragma unroll
@@ -685,11 +739,12 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
   const RowSource& src = a.src;
   const void* in = DOWN ? (bw.shared ? a.h_s : a.h) : (bw.shared && a.x_s ? a.x_s : a.x);
   void* out = DOWN ? (void*)(bw.shared ? a.y_s : a.y) : (bw.shared ? a.h_s : a.h);
-  // 16-byte granules on rows of >= 64 granules take the ring path (the
-  // launcher keeps blocks within kMaxRingRows rows); slices longer than one
-  // granule only occur on such rows, so the register path is compiled for
-  // one-granule slices and int2 only
-  constexpr bool kRingFmt = Fmt<WDT>::GB == 16;
+  // 16-byte granules (and int8's 32-byte ones, as two slots) on rows of >= 64
+  // granules take the ring path (the launcher keeps blocks within
+  // kMaxRingRows rows); slices longer than one granule only occur on such
+  // rows, so the register path is compiled for one-granule slices and int2
+  // only
+  constexpr bool kRingFmt = Fmt<WDT>::GB == 16 || WDT == MOE_I8;
   constexpr bool kChunk = !kRingFmt || KSL == Fmt<WDT>::EPG;
   constexpr int EPG = Fmt<WDT>::EPG, AB = ABF16 ? 2 : 4;
   const bool ring = kRingFmt && jb.lpr == 64;
@@ -776,7 +831,7 @@ template <int WR, int KR, int WS, int KS, bool DOWN>
 hipError_t gemv_go(const GemvArgs& a, int ntmax, int act_bf16, unsigned blocks, hipStream_t s) {
 #define MOE_K(NT, AB) \
   hipLaunchKernelGGL((k_gemv<WR, KR, WS, KS, NT, AB, DOWN>), dim3(blocks), dim3(kThreads), 0, s, a)
-  if constexpr (KR <= 32) {
+  if constexpr (KR <= 32 && WR != MOE_I8) {
     if (ntmax >= 2) {
       if (act_bf16) MOE_K(2, 1); else MOE_K(2, 0);
       return hipGetLastError();
@@ -794,6 +849,8 @@ hipError_t gemv_i4_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_i4_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_i2_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_i2_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
+hipError_t gemv_i8_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
+hipError_t gemv_i8_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_bf_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_bf_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 

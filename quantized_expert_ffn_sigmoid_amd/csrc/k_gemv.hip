@@ -28,6 +28,7 @@ bool make_geo(int dtype, int32_t K, MatGeo& g) {
   switch (dtype) {
     case MOE_I4: return geo_for<MOE_I4>(K, g);
     case MOE_I2: return geo_for<MOE_I2>(K, g);
+    case MOE_I8: return geo_for<MOE_I8>(K, g);
     case MOE_BF16: return geo_for<MOE_BF16>(K, g);
     default: return false;
   }
@@ -40,7 +41,8 @@ bool gemv_supported(int dtype, int32_t K) {
 
 bool gemv_ring(int dtype, int32_t K) {
   MatGeo g;
-  return (dtype == MOE_I4 || dtype == MOE_BF16) && make_geo(dtype, K, g) && g.lpr == 64;
+  return (dtype == MOE_I4 || dtype == MOE_I8 || dtype == MOE_BF16) && make_geo(dtype, K, g) &&
+         g.lpr == 64;
 }
 
 bool gemv_pair_supported(int dtype, int32_t K, int sdtype, int32_t Ks) {
@@ -52,7 +54,7 @@ bool gemv_pair_supported(int dtype, int32_t K, int sdtype, int32_t Ks) {
 }
 
 static int64_t row_bytes_of(int dtype, int K, bool pair) {
-  const int64_t bytes_x4 = dtype == MOE_I4 ? 2 : dtype == MOE_I2 ? 1 : 8;   // bytes per 4 elements
+  const int64_t bytes_x4 = dtype == MOE_I4 ? 2 : dtype == MOE_I2 ? 1 : dtype == MOE_I8 ? 4 : 8;
   return (int64_t)K * bytes_x4 / 4 * (pair ? 2 : 1);
 }
 
@@ -100,10 +102,11 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     shared_dtype = dtype;
   }
   // tokens one pass of the kernel takes (two only on short slices, where the
-  // second token's activations fit in registers); buckets that may hold more
+  // second token's activations fit in registers, and not with the 32-byte
+  // int8 granules, whose registers they would crowd out); buckets that may hold more
   // switch the launch to token mode, which splits them over blocks instead of
   // making one block pass over its rows again
-  const int ntmax = (a.geo.kc <= 32 && max_rows_per_slot >= 2) ? 2 : 1;
+  const int ntmax = (a.geo.kc <= 32 && dtype != MOE_I8 && max_rows_per_slot >= 2) ? 2 : 1;
   a.per_token = max_rows_per_slot > ntmax;
   if (a.per_token) {
     a.n_slots = a.src.routed ? a.n_tok * a.src.top_k : a.src.n_rows;
@@ -141,6 +144,7 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
   switch (dtype) {
     case MOE_I4: return (down ? gemv_i4_dn : gemv_i4_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
     case MOE_I2: return (down ? gemv_i2_dn : gemv_i2_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
+    case MOE_I8: return (down ? gemv_i8_dn : gemv_i8_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
     case MOE_BF16: return (down ? gemv_bf_dn : gemv_bf_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
     default: return hipErrorInvalidValue;
   }

@@ -54,7 +54,7 @@ hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, i
 }
 
 // Dequantized weights: out[r][c] = float(q) * scale[row0 + r] (one rounded
-// fp32 multiply); out_bf16 = bf16 bits of q (exact for |q| <= 8).
+// fp32 multiply); out_bf16 = bf16 bits of q (exact for |q| <= 256).
 __global__ __launch_bounds__(256) void k_dequant(int dtype, const uint8_t* __restrict__ codes,
                                                  const float* __restrict__ scales, int32_t cols,
                                                  int32_t row0, int32_t n_rows,
@@ -73,9 +73,11 @@ __global__ __launch_bounds__(256) void k_dequant(int dtype, const uint8_t* __res
     if (dtype == MOE_I4) {
       const uint32_t v = (codes[r * (cols / 2) + c / 2] >> (4 * (c & 1))) & 0xFu;
       q = (int)(v ^ 8u) - 8;
-    } else {
+    } else if (dtype == MOE_I2) {
       const uint32_t v = (codes[r * (cols / 4) + c / 4] >> (2 * (c & 3))) & 0x3u;
       q = (int)(v ^ 2u) - 2;
+    } else {
+      q = (int)(int8_t)codes[r * (int64_t)cols + c];
     }
     out[i] = __fmul_rn((float)q, scales[r]);
     if (out_bf16) out_bf16[i] = f32_to_bf16_bits((float)q);

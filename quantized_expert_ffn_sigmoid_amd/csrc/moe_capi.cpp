@@ -21,7 +21,9 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool dtype_is_weight(int32_t t) { return t == MOE_I4 || t == MOE_I2 || t == MOE_BF16; }
+bool dtype_is_weight(int32_t t) {
+  return t == MOE_I4 || t == MOE_I2 || t == MOE_I8 || t == MOE_BF16;
+}
 
 // Descriptor consistency (MOE_EINVAL) and kernel coverage (MOE_EUNSUPPORTED).
 // The decode-sized expert path (GEMV kernels) covers the layer's shapes.
@@ -35,7 +37,9 @@ bool gemv_layer_ok(const moe_layer_desc& d) {
   return true;
 }
 
-moe_status check_desc(const moe_layer_desc* d) {
+// layer: also require that one expert path covers the whole layer (routed
+// and shared sets together); single-expert calls check their own set only.
+moe_status check_desc(const moe_layer_desc* d, bool layer = true) {
   if (!d) return MOE_EINVAL;
   if (d->hidden <= 0 || d->inter <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
   if (d->top_k > d->n_experts) return MOE_EINVAL;
@@ -56,7 +60,7 @@ moe_status check_desc(const moe_layer_desc* d) {
   if (d->hidden % 32 != 0) return MOE_EUNSUPPORTED;
   // a layer is accepted when either expert path covers it; calls whose batch
   // size selects an uncovered path fail with MOE_EUNSUPPORTED
-  if (!gemv_layer_ok(*d) && !ggemm_supported(*d)) return MOE_EUNSUPPORTED;
+  if (layer && !gemv_layer_ok(*d) && !ggemm_supported(*d)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -320,14 +324,14 @@ moe_status check_layer_args(const moe_layer_desc* d, const moe_layer_weights* w)
 extern "C" {
 
 size_t moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens) {
-  if (check_desc(d) != MOE_OK || n_tokens < 0) return 0;
+  if (check_desc(d, false) != MOE_OK || n_tokens < 0) return 0;
   return carve(*d, n_tokens > 0 ? n_tokens : 1).total;
 }
 
 moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float* bias,
                      const void* x, int32_t n_tokens, int32_t* topk_idx, float* topk_w, void* ws,
                      size_t ws_bytes, void* stream) {
-  moe_status st = check_desc(d);
+  moe_status st = check_desc(d, false);   // routing only: no expert kernels involved
   if (st != MOE_OK) return st;
   if (n_tokens < 0) return MOE_EINVAL;
   if (n_tokens == 0) return MOE_OK;
@@ -365,7 +369,7 @@ moe_status moe_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const 
 moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, int32_t shared,
                           int32_t expert, const void* x, const int32_t* rows, int32_t n_rows,
                           int32_t row_div, float* y, void* ws, size_t ws_bytes, void* stream) {
-  moe_status st = check_desc(d);
+  moe_status st = check_desc(d, false);
   if (st != MOE_OK) return st;
   if (n_rows < 0 || row_div <= 0) return MOE_EINVAL;
   if (shared && (d->n_shared <= 0 || expert != 0)) return MOE_EINVAL;

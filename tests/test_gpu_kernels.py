@@ -55,7 +55,7 @@ def test_device_twin_is_bit_identical(c2_layers_i4_i2):
             assert np.array_equal(b2[off:off + a.size], a), (e, "int2", key)
 
 
-@pytest.mark.parametrize("dtype", [gen.I4, gen.I2, gen.BF16])
+@pytest.mark.parametrize("dtype", [gen.I4, gen.I2, gen.I8, gen.BF16])
 def test_dequant_bit_exact(dtype):
     cfg = gen.shrink(gen.get_config("c2"), hidden=512, inter=256)
     ex = gen.expert(cfg, 0, 5, dtype)
@@ -194,6 +194,9 @@ FFN_CASES = [
     ("c2", gen.I4, False, 200, 5, True),
     ("c2", gen.I4, True, 0, 2, False),
     ("c4", gen.I2, False, 9, 4, True),
+    ("c0", gen.I8, False, 5, 3, False),
+    ("c2", gen.I8, False, 33, 1, False),
+    ("c2", gen.I8, False, 150, 6, True),
     ("c1", gen.BF16, False, 5, 3, False),
     ("c3", gen.I4, False, 42, 37, True),
     ("c3", gen.I4, True, 0, 19, False),

@@ -41,6 +41,7 @@ def _oracle_layer(cfg, layer_idx, x, dtype=None, tokens=None):
 
 
 LAYER_CASES = [("c0", None, 1), ("c0", None, 3), ("c0", None, 7), ("c2", None, 1),
+               ("c2", gen.I8, 1), ("c2", gen.I8, 5),
                ("c2", None, 16), ("c4", gen.I4, 2), ("c4", gen.I2, 4), ("c4", gen.I4, 16),
                ("c4", gen.I2, 16),
                ("c1", None, 1), ("c1", None, 16)]
@@ -154,3 +155,51 @@ def test_stack_c4_8_layers(dtype, T):
     for l in range(cfg.n_layers):
         assert_close(gys[l], ys[l], False, f"free-running layer {l}")
     assert_close(gx, xf, False, "final residual stream")
+
+
+def _widened(hl4):
+    cfg = hl4.cfg
+    hl8 = gen.HostLayer(cfg=cfg, layer=hl4.layer, w_router=hl4.w_router, bias=hl4.bias,
+                        dtype=gen.I8)
+    for e in range(cfg.n_experts):
+        hl8.experts[e] = gen.expert_i8_from_i4(hl4.get(e), cfg.hidden, cfg.inter)
+    hl8.shared = hl4.shared
+    return hl8
+
+
+@pytest.mark.parametrize("act", [gen.F32, gen.BF16])
+def test_int8_container_of_int4_codes_bitwise(act):
+    """int4 codes re-packed into the int8 container give bit-identical layer
+    outputs on the GPU (the int8 kernels read each code as the operand the
+    int4 kernels read and accumulate in the same order), at the GLM layer's
+    widths (gate/up rows of 6144, down rows of 2048) on 16 experts."""
+    cfg = gen.shrink(gen.get_config("c2"), n_experts=16, top_k=4, n_group=4, topk_group=2,
+                     act_dtype=act, seed=44)
+    hl4 = gen.host_layer(cfg, 0, experts="all")
+    hl8 = _widened(hl4)
+    l4 = gdev.upload_host_layer(hl4, DEV)
+    l8 = gdev.upload_host_layer(hl8, DEV)
+    for T in (1, 2, 5, 16):
+        print_case("int8 vs int4 container", act, T)
+        x = gen.x_tokens(cfg, T, batch_id=60 + T)
+        o4, i4, w4 = _layer_gpu(l4, x)
+        o8, i8, w8 = _layer_gpu(l8, x)
+        assert np.array_equal(i4, i8) and np.array_equal(w4.view(np.uint32), w8.view(np.uint32))
+        assert np.array_equal(o4.view(np.uint32), o8.view(np.uint32)), f"T={T}"
+
+
+@pytest.mark.parametrize("T", [1, 4, 9])
+def test_int8_small_layer(T):
+    """The int8 container with full-range codes on a small layer whose shared
+    expert is int8 too (K-slices of one granule: the register path)."""
+    cfg = gen.shrink(gen.get_config("c0"), expert_dtype=gen.I8, shared_dtype=gen.I8,
+                     hidden=128, inter=64, seed=45)
+    hl = gen.host_layer(cfg, 0, experts="all")
+    layer = gdev.upload_host_layer(hl, DEV)
+    x = gen.x_tokens(cfg, T, batch_id=70 + T)
+    print_case("int8 small layer", T)
+    out, idx, w = _layer_gpu(layer, x)
+    ref, ridx, rw = oracle.layer_forward_host(hl, x)
+    assert np.array_equal(idx, ridx)
+    r = assert_close(out, ref, False, f"int8 small T={T}")
+    print(f"  max|err|/rms = {r:.3e}")

@@ -98,3 +98,41 @@ def test_dequant_integer_and_pow2_scales():
     got = oracle.dequant_rows(oracle.I4, packed, s, cols, 0, 8)
     exact = q.astype(np.float64) * s.astype(np.float64)[:, None]
     assert np.array_equal(got, exact.astype(np.float32))
+
+
+def test_int8_exhaustive():
+    """The int8 container: every byte decodes to its two's-complement value."""
+    allb = np.arange(256, dtype=np.uint8)
+    got = oracle.decode_codes(oracle.I8, allb, 256)
+    assert np.array_equal(got, allb.view(np.int8))
+    assert got.min() == -128 and got.max() == 127
+
+
+def test_int8_dequant_exact():
+    """q * s in float for int8 codes: integer and power-of-two scales make
+    every product exact, so the oracle's float multiply must reproduce them."""
+    codes = np.arange(256, dtype=np.uint8).reshape(4, 64)
+    scales = np.array([1.0, 0.5, 3.0, 2.0 ** -10], dtype=np.float32)
+    got = oracle.dequant_rows(oracle.I8, codes, scales, 64, 0, 4)
+    want = codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]
+    assert np.array_equal(got.astype(np.float64), want)
+
+
+def test_int8_widening_of_int4_codes():
+    """gen's int4 -> int8 re-packing keeps every code: decoding the int8
+    container gives the int4 container's codes."""
+    packed = gen.int4_codes(seed=5, layer=1, tensor=gen.T_DN_CODES, expert=2, rows=16, cols=256)
+    wide = gen.int8_from_int4(packed, 256)
+    assert wide.shape == (16, 256)
+    d4 = oracle.decode_codes(oracle.I4, packed, packed.size * 2)
+    d8 = oracle.decode_codes(oracle.I8, wide, wide.size)
+    assert np.array_equal(d4, d8)
+
+
+def test_int8_generator_range():
+    """Full-range int8 codes: symmetric on [-127, 127], every value drawn."""
+    c = gen.int8_codes(seed=3, layer=0, tensor=gen.T_GU_I8, expert=1, rows=64, cols=1024)
+    v = oracle.decode_codes(oracle.I8, c, c.size).astype(np.int64)
+    assert v.min() == -127 and v.max() == 127
+    assert len(np.unique(v)) == 255
+    assert abs(v.mean()) < 1.0

@@ -15,6 +15,8 @@ def _np_codes(packed, cols, dtype):
     if dtype == gen.I4:
         out[:, 0::2] = (packed << 4).astype(np.int8) >> 4
         out[:, 1::2] = packed.astype(np.int8) >> 4
+    elif dtype == gen.I8:
+        out[:] = packed.view(np.int8)
     else:
         for j in range(4):
             out[:, j::4] = (packed << (6 - 2 * j)).astype(np.int8) >> 6
@@ -72,6 +74,7 @@ def _dense_layer(cfg, hl, x64, idx, w64):
 SMALL = [
     dict(base="c0"),
     dict(base="c0", expert_dtype=gen.I2, hidden=128, inter=64),
+    dict(base="c0", expert_dtype=gen.I8, shared_dtype=gen.I8, hidden=128, inter=64),
     dict(base="c2", hidden=128, inter=64, n_experts=16, n_group=4, topk_group=2, top_k=4),
     dict(base="c3", hidden=128, inter=64, n_experts=16, n_group=4, topk_group=2, top_k=4),
     dict(base="c1", hidden=64, inter=32, n_experts=8, top_k=3),
@@ -162,3 +165,29 @@ def test_residual_add_is_float_addition():
     got = oracle.residual_add(x, y)
     want = x + y.astype(np.float32)
     assert np.array_equal(got, want)
+
+
+def widened_layer(hl4):
+    """The same layer with every int4 expert re-packed into the int8 container."""
+    cfg = hl4.cfg
+    hl8 = gen.HostLayer(cfg=cfg, layer=hl4.layer, w_router=hl4.w_router, bias=hl4.bias,
+                        dtype=gen.I8)
+    for e in range(cfg.n_experts):
+        hl8.experts[e] = gen.expert_i8_from_i4(hl4.get(e), cfg.hidden, cfg.inter)
+    hl8.shared = hl4.shared
+    return hl8
+
+
+@pytest.mark.parametrize("spec", [SMALL[0], SMALL[3]], ids=["c0", "c2small"])
+def test_int8_container_of_int4_codes_is_bitwise_identical(spec):
+    """The int8 container holding int4 codes (the pages validate the int4
+    packing bit-identical to the int8 container) defines the same layer: the
+    oracle's outputs agree bit for bit."""
+    cfg = _small_cfg(spec)
+    hl4 = gen.host_layer(cfg, 0, experts="all")
+    hl8 = widened_layer(hl4)
+    x = gen.x_tokens(cfg, 6, batch_id=2)
+    o4, i4, w4 = oracle.layer_forward_host(hl4, x)
+    o8, i8, w8 = oracle.layer_forward_host(hl8, x)
+    assert np.array_equal(i4, i8) and np.array_equal(w4, w8)
+    assert np.array_equal(o4.view(np.uint64), o8.view(np.uint64))
