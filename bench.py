@@ -214,7 +214,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c2", choices=["c2", "c4i4", "c4i2", "c3", "c1", "c0"])
+    ap.add_argument("--workload", default="c2",
+                    choices=["c2", "c2i8", "c4i4", "c4i2", "c3", "c1", "c0"])
     ap.add_argument("--batch", type=int, default=None, help="tokens per step (c4: 2, 4 or 16)")
     ap.add_argument("--layers", type=int, default=8, help="distinct layer instances rotated")
     ap.add_argument("--eager", action="store_true", help="launch each step eagerly (no graph)")
@@ -249,13 +250,16 @@ def main():
     dev = torch.device("cuda:0")
     hip = Hip()
     wl = args.workload
-    base = {"c2": "c2", "c4i4": "c4", "c4i2": "c4", "c3": "c3", "c1": "c1", "c0": "c0"}[wl]
+    base = {"c2": "c2", "c2i8": "c2", "c4i4": "c4", "c4i2": "c4", "c3": "c3", "c1": "c1",
+            "c0": "c0"}[wl]
     cfg = gen.get_config(base)
-    dtype = {"c4i2": gen.I2}.get(wl, cfg.expert_dtype)
+    dtype = {"c4i2": gen.I2, "c2i8": gen.I8}.get(wl, cfg.expert_dtype)
     T = args.batch or (16 if base == "c4" else cfg.batches[0])
     L = args.layers if base in ("c2", "c3", "c4") else 1
     if base == "c3":
         L = min(L, 2)
+    if dtype == gen.I8:
+        L = min(L, 4)   # 4 int8 layers hold as many bytes as 8 int4 ones (~39 GB)
 
     # ---- inputs, resident in HBM before timing
     if base in ("c0", "c1"):
@@ -396,7 +400,7 @@ def main():
         "config": {
             "workload": f"{cfg.name}: H={cfg.hidden} I={cfg.inter} E={cfg.n_experts} "
                         f"top-{cfg.top_k} ({'softmax' if cfg.router else 'sigmoid noaux_tc'}) "
-                        f"{ {gen.I4: 'int4', gen.I2: 'int2', gen.BF16: 'bf16'}[dtype]} experts, "
+                        f"{ {gen.I4: 'int4', gen.I2: 'int2', gen.I8: 'int8', gen.BF16: 'bf16'}[dtype]} experts, "
                         f"{T} token(s)/step, {L} rotating layer instance(s)",
             "global_batch": T,
             "seq_len": 1,

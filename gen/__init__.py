@@ -66,6 +66,7 @@ class Config:
     bf16_std: float = 0.02
     zipf_s: float = 1.1
     zipf_lambda: float = 0.0
+    top_p: float = 0.0             # adaptive expert top-p (0: off)
 
 
 # Router bias of the Zipf-skewed workload, by popularity rank: calibrated once

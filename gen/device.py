@@ -85,7 +85,7 @@ class DeviceLayer:
             pass
         s = _S()
         for k in ("hidden", "inter", "n_experts", "top_k", "router", "n_group", "topk_group",
-                  "routed_scaling", "act_dtype", "n_shared", "shared_dtype"):
+                  "routed_scaling", "act_dtype", "n_shared", "shared_dtype", "top_p"):
             setattr(s, k, getattr(c, k))
         s.expert_dtype = self.expert_dtype
         s.norm_eps = c.norm_eps or 0.0

@@ -78,6 +78,15 @@ typedef struct {
   int32_t n_shared;        /* 0 or 1 shared expert (intermediate size n_shared * I)   */
   int32_t shared_dtype;    /* MOE_I4 | MOE_I2 | MOE_I8 | MOE_BF16                     */
   float norm_eps;          /* RMSNorm epsilon used by moe_stack_forward               */
+  float top_p;             /* adaptive expert top-p ("colibri" README, "Quick start" */
+                           /* knob --topp): 0 (or >= 1) = off; 0 < top_p < 1 keeps, */
+                           /* per token, the shortest rank prefix of the top_k      */
+                           /* whose routing mass reaches top_p of their total (at   */
+                           /* least one expert) and renormalizes its weights;       */
+                           /* dropped slots get topk_idx -1 and topk_w 0.  Masses:  */
+                           /* the sigmoid values (softmax: exp(z - z_max)), summed  */
+                           /* in rank order in fp64; slot j stays when the mass     */
+                           /* before it is < top_p * total.  NaN or < 0: MOE_EINVAL */
 } moe_layer_desc;
 
 /* One expert set: E routed experts, or the n_shared shared expert(s).
@@ -119,8 +128,8 @@ size_t moe_workspace_bytes(const moe_layer_desc* d, int32_t n_tokens);
  * Softmax top-k (Granite MoE layer, "Glacial" page): the top_k largest z are
  * chosen; topk_w = softmax over the chosen z, times routed_scaling.
  * x: [n_tokens][H] of act_dtype.  Outputs: topk_idx [n_tokens][k] int32,
- * topk_w [n_tokens][k] fp32.  Errors: MOE_EINVAL (bad descriptor or pointer),
- * MOE_EWORKSPACE. */
+ * topk_w [n_tokens][k] fp32 (with top_p, dropped slots: -1 and 0).  Errors:
+ * MOE_EINVAL (bad descriptor or pointer), MOE_EWORKSPACE. */
 moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float* bias,
                      const void* x, int32_t n_tokens, int32_t* topk_idx, float* topk_w,
                      void* ws, size_t ws_bytes, void* stream);
@@ -131,9 +140,10 @@ moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float
  *   entries[F]   the slots f, sorted by (expert, f);  inverse[F]: inverse[entries[p]] = p;
  *   active[E]    experts with counts > 0, ascending (first n_active entries valid);
  *   n_active[1]  their number.  F = n_tokens * top_k.
- * Indices outside [0, E) are a caller error (MOE_EINVAL is not detectable on
- * the host: such slots are dropped from every output).  ws/ws_bytes are
- * unused (pass NULL/0). */
+ * Index -1 marks a slot dropped by adaptive top-p: it is left out of every
+ * output and its inverse is -1.  Other indices outside [0, E) are a caller
+ * error (not detectable on the host: such slots are treated the same way).
+ * ws/ws_bytes are unused (pass NULL/0). */
 moe_status moe_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t* topk_idx,
                       int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
                       int32_t* active, int32_t* n_active, void* ws, size_t ws_bytes, void* stream);

@@ -32,7 +32,8 @@ class _Desc(ctypes.Structure):
                 ("router", ctypes.c_int32), ("n_group", ctypes.c_int32),
                 ("topk_group", ctypes.c_int32), ("routed_scaling", ctypes.c_double),
                 ("expert_dtype", ctypes.c_int32), ("act_bf16", ctypes.c_int32),
-                ("n_shared", ctypes.c_int32), ("shared_dtype", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("shared_dtype", ctypes.c_int32),
+                ("top_p", ctypes.c_double)]
 
 
 class _Set(ctypes.Structure):
@@ -56,6 +57,7 @@ class Desc:
     act_bf16: int = 0
     n_shared: int = 0
     shared_dtype: int = BF16
+    top_p: float = 0.0      # adaptive expert top-p (off unless 0 < top_p < 1)
 
     @staticmethod
     def from_config(cfg, expert_dtype: Optional[int] = None) -> "Desc":
@@ -64,12 +66,12 @@ class Desc:
                     topk_group=cfg.topk_group, routed_scaling=float(cfg.routed_scaling),
                     expert_dtype=cfg.expert_dtype if expert_dtype is None else expert_dtype,
                     act_bf16=1 if cfg.act_dtype == BF16 else 0, n_shared=cfg.n_shared,
-                    shared_dtype=cfg.shared_dtype)
+                    shared_dtype=cfg.shared_dtype, top_p=float(np.float32(cfg.top_p)))
 
     def c(self) -> _Desc:
         return _Desc(self.hidden, self.inter, self.n_experts, self.top_k, self.router,
                      self.n_group, self.topk_group, self.routed_scaling, self.expert_dtype,
-                     self.act_bf16, self.n_shared, self.shared_dtype)
+                     self.act_bf16, self.n_shared, self.shared_dtype, self.top_p)
 
 
 _lib = None

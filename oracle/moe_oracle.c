@@ -31,13 +31,20 @@
  * RMSNorm output and residual stream to float.
  *
  * Parity status (what pins each function; the tests under tests/ hold them):
- *   orc_decode_codes     exhaustive round trip over all bytes; worked bytes.
+ *   orc_decode_codes     exhaustive round trip over all bytes (int4, int2,
+ *                        int8); worked bytes; int4 codes re-packed as int8
+ *                        decode to the same values.
  *   orc_dequant_rows     integer and power-of-two scale cases, exact.
  *   orc_logits           one-hot and small-integer inputs (exact matmul).
  *   orc_select           brute-force subset search on small E, exact ties,
- *                        reductions to plain top-k, closed-form weights.
+ *                        reductions to plain top-k, closed-form weights;
+ *                        adaptive top-p: a worked example with exact masses,
+ *                        off values equal the plain router, kept set a prefix
+ *                        with minimal sufficient mass, weights proportional
+ *                        and summing to the scaling, monotone in top_p.
  *   orc_route            = orc_logits + orc_select.
- *   orc_bucket           numpy stable argsort; permutation invariants.
+ *   orc_bucket           numpy stable argsort; permutation invariants;
+ *                        dropped slots (-1) left out, inverse -1.
  *   orc_layer_band       a test tolerance, not part of the layer: zero for f32
  *                        activations and for a zero window, monotone in the
  *                        window, and equal to the sum over every h at the
@@ -45,7 +52,9 @@
  *   orc_expert_ffn       worked H=2,I=1 example; integer-matrix case against
  *                        numpy matmul and scipy's logistic; scale factoring.
  *   orc_layer_forward    dense evaluation of all experts; batch-union equals
- *                        per-token; x=0; E=1,k=1; token permutation.
+ *                        per-token; x=0; E=1,k=1; token permutation; the
+ *                        int8 container of int4 codes gives the same bits;
+ *                        with top-p, the sum over the kept experts.
  *   orc_rmsnorm          closed-form rms of the output.
  *   orc_residual_add     f32 addition, exact cases.
  *
@@ -163,6 +172,7 @@ static int desc_ok(const orc_desc* d) {
   } else if (d->router != ORC_ROUTER_SOFTMAX_TOPK) {
     return 0;
   }
+  if (!(d->top_p >= 0.0)) return 0;   /* also rejects NaN */
   return 1;
 }
 
@@ -206,7 +216,15 @@ static int argbest(const double* v, const unsigned char* allowed, int n) {
  * s / sum(s) over the chosen, times routed_scaling.
  * Softmax top-k (the Granite MoE layer of the "Glacial" page): the top_k
  * largest logits are chosen and their weights are the softmax over those k.
- * Ties go to the lowest index everywhere; output is in rank order. */
+ * Ties go to the lowest index everywhere; output is in rank order.
+ * Adaptive expert top-p ("colibri" README, "Quick start" knobs: --topp; the
+ * pages give the knob and its effect, fewer experts read, not the rule; ours
+ * is the nucleus rule over the chosen experts): with 0 < top_p < 1, only the
+ * shortest rank prefix whose routing mass reaches top_p of the total is kept
+ * -- slot j stays when the mass of the slots before it is below top_p times
+ * the total, so at least one -- and the kept weights are renormalized over
+ * the prefix; dropped slots get index -1 and weight 0.  Masses are the
+ * sigmoid values (or softmax numerators), summed in rank order in double. */
 static void select_one(const orc_desc* d, const double* z, const float* bias, int32_t* idx,
                        float* w, double* w64) {
   const int E = d->n_experts, K = d->top_k;
@@ -228,7 +246,6 @@ static void select_one(const orc_desc* d, const double* z, const float* bias, in
       wk[j] = exp(z[idx[j]] - z0);
       wsum += wk[j];
     }
-    for (int j = 0; j < K; ++j) wk[j] = wk[j] / wsum * d->routed_scaling;
   } else {
     const int G = d->n_group, per = E / G;
     for (int e = 0; e < E; ++e) {
@@ -262,10 +279,29 @@ static void select_one(const orc_desc* d, const double* z, const float* bias, in
       idx[j] = b;
       cand[b] = 0;
     }
-    for (int j = 0; j < K; ++j) wsum += s[idx[j]];
-    for (int j = 0; j < K; ++j) wk[j] = s[idx[j]] / wsum * d->routed_scaling;
+    for (int j = 0; j < K; ++j) {
+      wk[j] = s[idx[j]];
+      wsum += wk[j];
+    }
     free(gscore);
     free(gallow);
+  }
+  /* wk[j]: the routing mass of rank j; wsum: their sum in rank order */
+  int keep = K;
+  if (d->top_p > 0.0 && d->top_p < 1.0) {
+    const double thr = d->top_p * wsum;
+    double before = 0.0;
+    keep = 0;
+    while (keep < K && before < thr) before += wk[keep++];
+    wsum = before;
+  }
+  for (int j = 0; j < K; ++j) {
+    if (j < keep) {
+      wk[j] = wk[j] / wsum * d->routed_scaling;
+    } else {
+      idx[j] = -1;
+      wk[j] = 0.0;
+    }
   }
   for (int j = 0; j < K; ++j) {
     if (w) w[j] = (float)wk[j];
@@ -304,7 +340,9 @@ int orc_route(const orc_desc* d, const float* w_router, const float* bias, const
 
 /* Batch-union grouping ("colibri" README, "What's implemented": each unique
  * expert of the batch is read once and applied to every position routed to
- * it): a stable counting sort of the flat slots f = t*top_k + j by expert. */
+ * it): a stable counting sort of the flat slots f = t*top_k + j by expert.
+ * Slots dropped by adaptive top-p (index -1) are not grouped; their inverse is
+ * -1. */
 int orc_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t* topk_idx,
                int32_t* counts, int32_t* offsets, int32_t* entries, int32_t* inverse,
                int32_t* active, int32_t* n_active) {
@@ -312,6 +350,7 @@ int orc_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t
   for (int e = 0; e < n_experts; ++e) counts[e] = 0;
   for (int64_t f = 0; f < F; ++f) {
     int e = topk_idx[f];
+    if (e == -1) continue;
     if (e < 0 || e >= n_experts) return ORC_EINVAL;
     counts[e] += 1;
   }
@@ -321,6 +360,10 @@ int orc_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t
   for (int e = 0; e < n_experts; ++e) fill[e] = offsets[e];
   for (int64_t f = 0; f < F; ++f) {
     int e = topk_idx[f];
+    if (e == -1) {
+      inverse[f] = -1;
+      continue;
+    }
     entries[fill[e]] = (int32_t)f;
     inverse[f] = fill[e];
     fill[e] += 1;
@@ -457,6 +500,7 @@ int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
     for (int64_t c = 0; c < H; ++c) xv[c] = x_at(x, 1, t * H + c);
     for (int64_t j = 0; j < K && rc == ORC_OK; ++j) {
       const int32_t e = idx[t * K + j];
+      if (e < 0) continue;   /* dropped by adaptive top-p */
       if (!set_has(routed, e)) {
         rc = ORC_EMISSING;
         break;
@@ -505,6 +549,7 @@ int orc_layer_forward_per_token(const orc_desc* d, const float* w_router, const 
   for (int64_t t = 0; t < n_tokens && rc == ORC_OK; ++t) {
     for (int64_t o = 0; o < H; ++o) acc[o] = 0.0;
     for (int64_t j = 0; j < K && rc == ORC_OK; ++j) {
+      if (idx[t * K + j] < 0) continue;   /* dropped by adaptive top-p */
       rc = ffn_token(d, routed, idx[t * K + j], d->inter, x, t, xv, hb, yj);
       for (int64_t o = 0; o < H; ++o) acc[o] += w64[t * K + j] * yj[o];
     }
@@ -560,7 +605,8 @@ int orc_layer_forward(const orc_desc* d, const float* w_router, const float* bia
   for (int64_t t = 0; t < n_tokens && rc == ORC_OK; ++t) {
     for (int64_t o = 0; o < H; ++o) {
       double acc = 0.0;
-      for (int64_t j = 0; j < K; ++j) acc += w64[t * K + j] * Y[(t * K + j) * H + o];
+      for (int64_t j = 0; j < K; ++j)
+        if (idx[t * K + j] >= 0) acc += w64[t * K + j] * Y[(t * K + j) * H + o];
       out[t * H + o] = acc;
     }
     if (d->n_shared > 0) {

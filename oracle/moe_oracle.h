@@ -27,6 +27,7 @@ typedef struct {
   int32_t act_bf16;           /* 1: x is bf16 and h is rounded to bf16          */
   int32_t n_shared;           /* 0 or 1                                         */
   int32_t shared_dtype;       /* ORC_BF16 | ORC_I4 | ORC_I2 | ORC_I8            */
+  double top_p;               /* adaptive expert top-p; off unless 0 < p < 1    */
 } orc_desc;
 
 /* One expert set.  Each table has one entry per expert; an entry may be NULL

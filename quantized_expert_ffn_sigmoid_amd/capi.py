@@ -35,7 +35,7 @@ class MoeLayerDesc(ctypes.Structure):
                 ("topk_group", ctypes.c_int32), ("routed_scaling", ctypes.c_float),
                 ("expert_dtype", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
                 ("n_shared", ctypes.c_int32), ("shared_dtype", ctypes.c_int32),
-                ("norm_eps", ctypes.c_float)]
+                ("norm_eps", ctypes.c_float), ("top_p", ctypes.c_float)]
 
 
 class MoeExpertSet(ctypes.Structure):
@@ -194,7 +194,7 @@ def make_desc(spec) -> MoeLayerDesc:
                         topk_group=g("topk_group"), routed_scaling=g("routed_scaling"),
                         expert_dtype=g("expert_dtype"), act_dtype=g("act_dtype"),
                         n_shared=g("n_shared"), shared_dtype=g("shared_dtype"),
-                        norm_eps=g("norm_eps", None) or 0.0)
+                        norm_eps=g("norm_eps", None) or 0.0, top_p=g("top_p", None) or 0.0)
 
 
 def make_set(p: Optional[dict]) -> MoeExpertSet:

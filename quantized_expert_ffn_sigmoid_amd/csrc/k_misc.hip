@@ -4,11 +4,13 @@
 
 namespace moe {
 
-// out[t][o] = sum_j w[t][j] * Y[t*K + j][o] (j ascending) + S[t][o]
+// out[t][o] = sum_j w[t][j] * Y[t*K + j][o] (j ascending, slots with index
+// -1 skipped) + S[t][o]
 // ("colibri" README, "What's implemented": routed_scaling_factor-weighted
 // combine with a shared expert; the scaling is already inside w).
 // With a residual: y_copy (optional) = the MoE output, out = residual + it.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
+                                                 const int32_t* __restrict__ topk_idx,
                                                  const float* __restrict__ topk_w,
                                                  const float* __restrict__ S, int32_t K,
                                                  int32_t H, const float* __restrict__ residual,
@@ -19,6 +21,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
   if (o >= H) return;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < K; ++j) {
+    if (topk_idx[t * K + j] < 0) continue;   // dropped by adaptive top-p: no Y row
     const float w = topk_w[t * K + j];
     const float4 y = *reinterpret_cast<const float4*>(Y + (t * K + j) * H + o);
     acc.x = fmaf(w, y.x, acc.x);
@@ -44,12 +47,13 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
   *reinterpret_cast<float4*>(out + t * H + o) = acc;
 }
 
-hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, int32_t T,
-                          int32_t K, int32_t H, const float* residual, float* out,
-                          float* y_copy, hipStream_t s) {
+hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* topk_w,
+                          const float* S, int32_t T, int32_t K, int32_t H, const float* residual,
+                          float* out, float* y_copy, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   const dim3 grid((H / 4 + 255) / 256, T);
-  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, Y, topk_w, S, K, H, residual, out, y_copy);
+  hipLaunchKernelGGL(k_combine, grid, dim3(256), 0, s, Y, topk_idx, topk_w, S, K, H, residual,
+                     out, y_copy);
   return hipGetLastError();
 }
 

@@ -245,6 +245,7 @@ static SelectParams select_params(const moe_layer_desc& d) {
   p.G = p.softmax ? 1 : d.n_group;
   p.topk_group = p.softmax ? 1 : d.topk_group;
   p.scaling = d.routed_scaling;
+  p.top_p = (double)d.top_p;
   return p;
 }
 

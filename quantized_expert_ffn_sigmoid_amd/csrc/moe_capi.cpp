@@ -54,6 +54,7 @@ moe_status check_desc(const moe_layer_desc* d, bool layer = true) {
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_EINVAL;
   if (d->n_shared < 0 || d->n_shared > 1) return MOE_EINVAL;
   if (d->n_shared > 0 && !dtype_is_weight(d->shared_dtype)) return MOE_EINVAL;
+  if (!(d->top_p >= 0.0f)) return MOE_EINVAL;   // also rejects NaN
   // kernel coverage
   if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_EUNSUPPORTED;
   if (d->router == MOE_ROUTER_SIGMOID_NOAUX_TC && d->n_group > 64) return MOE_EUNSUPPORTED;
@@ -261,7 +262,7 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     MOE_TRY(launch_ggemm(q, true, d.expert_dtype, d.shared_dtype, s));
     record(opts, MOE_STAGE_DOWN, 1, s);
     record(opts, MOE_STAGE_COMBINE, 0, s);
-    MOE_TRY(launch_combine(Y, tw, has_sh ? S : nullptr, T, K, H, residual, out, y_copy, s));
+    MOE_TRY(launch_combine(Y, idx, tw, has_sh ? S : nullptr, T, K, H, residual, out, y_copy, s));
     record(opts, MOE_STAGE_COMBINE, 1, s);
     return MOE_OK;
   }
@@ -300,7 +301,8 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   record(opts, MOE_STAGE_DOWN, 1, s);
 
   record(opts, MOE_STAGE_COMBINE, 0, s);
-  MOE_TRY(launch_combine(Y, tw, d.n_shared > 0 ? S : nullptr, T, K, H, residual, out, y_copy, s));
+  MOE_TRY(launch_combine(Y, idx, tw, d.n_shared > 0 ? S : nullptr, T, K, H, residual, out, y_copy,
+                         s));
   record(opts, MOE_STAGE_COMBINE, 1, s);
   return MOE_OK;
 }

@@ -175,9 +175,9 @@ hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const 
                                 int32_t* active, int32_t* n_active, hipStream_t s);
 // out[t] = sum_j w[t][j] * Y[t*k + j] + (S ? S[t] : 0) (+ residual[t] when given;
 // then y_copy[t] receives the MoE output without the residual).
-hipError_t launch_combine(const float* Y, const float* topk_w, const float* S, int32_t T,
-                          int32_t K, int32_t H, const float* residual, float* out,
-                          float* y_copy, hipStream_t s);
+hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* topk_w,
+                          const float* S, int32_t T, int32_t K, int32_t H, const float* residual,
+                          float* out, float* y_copy, hipStream_t s);
 hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);

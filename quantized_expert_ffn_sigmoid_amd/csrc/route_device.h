@@ -107,6 +107,7 @@ __device__ __forceinline__ void wave_top2(double& a, double& b) { segment_top2(a
 struct SelectParams {
   int32_t E, K, G, topk_group, softmax;
   float scaling;
+  double top_p;   // adaptive expert top-p, active when 0 < top_p < 1
 };
 
 // Selection for one token by one wave: zt = the token's E logits; writes its
@@ -197,9 +198,10 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     }
   }
 
-  // top-k among the open experts, in rank order
+  // top-k among the open experts, in rank order; lane j keeps rank j's mass
+  // and the mass of the ranks before it (for adaptive top-p)
   int my_idx = 0;
-  double my_s = 0.0, ssum = 0.0, z0 = 0.0;
+  double my_s = 0.0, my_before = 0.0, ssum = 0.0, z0 = 0.0;
   for (int j = 0; j < p.K; ++j) {
     // the lane's best: ascending experts, so a strictly larger value wins
     // and equal values keep the lower index
@@ -226,14 +228,27 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     } else {
       contrib = s_win;
     }
+    my_before = lane == j ? ssum : my_before;
     ssum += contrib;   // sequential sum in rank order
     my_idx = lane == j ? ri : my_idx;
     my_s = lane == j ? contrib : my_s;
   }
+  // adaptive top-p: rank j stays when the mass before it is below top_p of
+  // the total; the kept prefix's mass (the mass before the first dropped
+  // rank) renormalizes the weights
+  bool keep = true;
+  double kept_sum = ssum;
+  if (p.top_p > 0.0 && p.top_p < 1.0) {
+    const double thr = p.top_p * ssum;
+    keep = my_before < thr;
+    const uint64_t kb = __ballot(lane < p.K && keep);
+    const int m = __popcll(kb);   // a prefix: the masses are nonnegative
+    if (m < p.K) kept_sum = readlane_d(my_before, m);
+  }
   if (lane < p.K) {
-    idx_out[lane] = my_idx;
-    w_out[lane] = (float)(my_s / ssum * (double)p.scaling);
-    if (idx_lds) idx_lds[lane] = my_idx;
+    idx_out[lane] = keep ? my_idx : -1;
+    w_out[lane] = keep ? (float)(my_s / kept_sum * (double)p.scaling) : 0.0f;
+    if (idx_lds) idx_lds[lane] = keep ? my_idx : -1;
   }
 }
 
@@ -305,10 +320,9 @@ __device__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx
   __syncthreads();
   for (int f = tid; f < F; f += nth) {
     const int key = s_key[f];
-    if (key < 0) continue;
-    const int pos = s_off[key] + s_rank[f];
-    entries[pos] = f;
-    inverse[f] = pos;
+    const int pos = key < 0 ? -1 : s_off[key] + s_rank[f];
+    if (key >= 0) entries[pos] = f;
+    inverse[f] = pos;   // -1 for a dropped slot
   }
 }
 
@@ -390,6 +404,8 @@ __device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx
       for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
       entries[pos] = (int32_t)f;
       inverse[f] = pos;
+    } else if (f < F) {
+      inverse[f] = -1;   // a dropped slot
     }
     __syncthreads();
     if (leader) {

@@ -78,7 +78,7 @@ def test_dequant_bit_exact(dtype):
 def _desc(cfg, dtype=None):
     spec = type("S", (), {})()
     for k in ("hidden", "inter", "n_experts", "top_k", "router", "n_group", "topk_group",
-              "routed_scaling", "act_dtype", "n_shared", "shared_dtype"):
+              "routed_scaling", "act_dtype", "n_shared", "shared_dtype", "top_p"):
         setattr(spec, k, getattr(cfg, k))
     spec.expert_dtype = cfg.expert_dtype if dtype is None else dtype
     spec.norm_eps = cfg.norm_eps or 0.0
@@ -121,6 +121,26 @@ def test_route_bit_exact(name, T):
     assert np.allclose(w, rw, rtol=1e-6, atol=0)
 
 
+TOPP_ROUTE_CASES = [("c2", 1, 0.7), ("c2", 16, 0.5), ("c2", 77, 0.9), ("c1", 16, 0.6),
+                    ("c3", 2048, 0.7), ("c0", 5, 0.3)]
+
+
+@pytest.mark.parametrize("name,T,p", TOPP_ROUTE_CASES)
+def test_route_top_p_bit_exact(name, T, p):
+    """Adaptive expert top-p: the kept prefix (indices, -1 for dropped slots)
+    bit-exact, the renormalized weights to the float rounding of the oracle's."""
+    cfg = gen.get_config(name, top_p=p)
+    print_case("route top-p", name, T, p)
+    w_r, bias = gen.router(cfg)
+    x = gen.x_tokens(cfg, T, batch_id=T + 5)
+    idx, w = route_on_gpu(cfg, w_r, bias, x)
+    ridx, rw, _ = oracle.route(oracle.Desc.from_config(cfg), w_r, bias, x, T)
+    assert (ridx < 0).any() or p >= 0.9
+    assert np.array_equal(idx, ridx)
+    assert np.allclose(w, rw, rtol=1e-6, atol=0)
+    assert (w[idx < 0] == 0).all()
+
+
 @pytest.mark.parametrize("name", ["c0", "c2", "c1"])
 def test_route_exact_ties(name):
     cfg = gen.get_config(name)
@@ -143,6 +163,31 @@ def test_route_exact_ties(name):
 
 BUCKET_CASES = [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (7, 2, 8), (33, 5, 1000), (0, 8, 256),
                 (1, 1, 1), (300, 4, 3)]
+# slots dropped by adaptive top-p (index -1): small and large slot counts
+BUCKET_DROP_CASES = [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (33, 5, 1000)]
+
+
+@pytest.mark.parametrize("T,K,E", BUCKET_DROP_CASES)
+def test_bucket_dropped_slots_bit_exact(T, K, E):
+    print_case("bucket dropped", T, K, E)
+    rng = np.random.default_rng(T * 7 + K)
+    idx = np.stack([rng.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    keep = rng.integers(1, K + 1, size=T)   # a kept prefix per token
+    idx[np.arange(K)[None, :] >= keep[:, None]] = -1
+    ref = oracle.bucket(idx, E)
+    F = T * K
+    n = int(ref["offsets"][-1])
+    dev = lambda m: torch.full((max(m, 1),), -7, dtype=torch.int32, device=DEV)
+    counts, offsets, entries, inverse, active, na = dev(E), dev(E + 1), dev(F), dev(F), dev(E), dev(1)
+    capi.moe_bucket(T, K, E, torch.from_numpy(idx.ravel().copy()).to(DEV), counts, offsets,
+                    entries, inverse, active, na)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    assert int(na.cpu().item()) == ref["n_active"]
+    assert np.array_equal(active.cpu().numpy()[:ref["n_active"]], ref["active"])
+    assert np.array_equal(entries.cpu().numpy()[:n], ref["entries"][:n])
+    assert np.array_equal(inverse.cpu().numpy(), ref["inverse"])
 
 
 @pytest.mark.parametrize("T,K,E", BUCKET_CASES)

@@ -203,3 +203,22 @@ def test_int8_small_layer(T):
     assert np.array_equal(idx, ridx)
     r = assert_close(out, ref, False, f"int8 small T={T}")
     print(f"  max|err|/rms = {r:.3e}")
+
+
+TOPP_LAYER_CASES = [("c2", 1, 0.7), ("c2", 4, 0.5), ("c4", 16, 0.6)]
+
+
+@pytest.mark.parametrize("name,T,p", TOPP_LAYER_CASES)
+def test_layer_top_p(name, T, p):
+    """The layer with adaptive expert top-p against the oracle: routing
+    bit-exact (dropped slots included), outputs within tolerance."""
+    cfg = gen.get_config(name, top_p=p)
+    print_case("layer top-p", name, T, p)
+    layer = gdev.generate_device_layer(cfg, 0, DEV)
+    x = gen.x_tokens(cfg, T, batch_id=300 + T)
+    out, idx, w = _layer_gpu(layer, x)
+    ref, ridx, rw = _oracle_layer(cfg, 0, x)
+    assert np.array_equal(idx, ridx) and (idx < 0).any()
+    assert np.allclose(w, rw, rtol=1e-6, atol=0)
+    r = assert_close(out, ref, cfg.act_dtype == gen.BF16, f"layer top-p {name} T={T}")
+    print(f"  max|err|/rms = {r:.3e}, experts kept {int((idx >= 0).sum())} of {idx.size}")

@@ -19,9 +19,12 @@ MUTANTS = {
     "int4_unsigned": ("return v >= 8 ? v - 16 : v;", "return v;"),
     "int2_crumb_order": ("(p[i / 4] >> (2 * (int)(i % 4)))", "(p[i / 4] >> (2 * (int)(3 - i % 4)))"),
     "group_score_max_only": ("gscore[g] = (b < 0) ? c[a] : c[a] + c[b];", "gscore[g] = c[a];"),
-    "bias_in_weights": ("for (int j = 0; j < K; ++j) wsum += s[idx[j]];", "for (int j = 0; j < K; ++j) { s[idx[j]] = c[idx[j]]; wsum += s[idx[j]]; }"),
+    "bias_in_weights": ("      wk[j] = s[idx[j]];\n", "      wk[j] = c[idx[j]];\n"),
     "ties_to_highest": ("return va > vb || (va == vb && ia < ib);", "return va > vb || (va == vb && ia > ib);"),
-    "no_scaling": ("wk[j] = s[idx[j]] / wsum * d->routed_scaling;", "wk[j] = s[idx[j]] / wsum;"),
+    "no_scaling": ("wk[j] = wk[j] / wsum * d->routed_scaling;", "wk[j] = wk[j] / wsum;"),
+    "topp_no_renormalization": ("    wsum = before;\n", "\n"),
+    "topp_one_expert_short": ("while (keep < K && before < thr) before += wk[keep++];", "while (keep < K && before + wk[keep] < thr) before += wk[keep++];"),
+    "int8_unsigned": ("return v >= 128 ? v - 256 : v;", "return v;"),
     "sigmoid_sign": ("s[e] = 1.0 / (1.0 + exp(-z[e]));", "s[e] = 1.0 / (1.0 + exp(z[e]));"),
     "silu_sign": ("double h = g / (1.0 + exp(-g)) * u;", "double h = g / (1.0 + exp(g)) * u;"),
     "gate_up_swapped": ("double h = g / (1.0 + exp(-g)) * u;", "double h = u / (1.0 + exp(-u)) * g;"),
