@@ -208,6 +208,64 @@ def cpu_baseline(cfg, dtype, T, seconds, max_tokens=256):
                        f"oracle layer forward timed for {spent:.1f} s")
 
 
+# -------------------------------------------------------- requantization
+def bench_requant(args):
+    """FP8 (E4M3, 128x128 block scales) -> int4 requantization of GLM-shaped
+    experts (gate/up [2I][H] and down [H][I] of 16 experts, stacked), with
+    the inputs resident in HBM; a step requantizes them all."""
+    import torch
+    from quantized_expert_ffn_sigmoid_amd import capi
+    dev = torch.device("cuda:0")
+    hip = Hip()
+    cfg = gen.get_config("c2")
+    H, I, NE, blk = cfg.hidden, cfg.inter, 16, 128
+    mats = []
+    for rows, cols in ((NE * 2 * I, H), (NE * H, I)):
+        g = torch.Generator(device=dev).manual_seed(rows)
+        fp8 = torch.randn((rows, cols), device=dev, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+        bs = torch.rand(((rows + blk - 1) // blk, (cols + blk - 1) // blk), device=dev,
+                        generator=g) * 2.0 ** -6 + 2.0 ** -12
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty(rows, dtype=torch.float32, device=dev)
+        mats.append((fp8, bs, rows, cols, codes, scales))
+    stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
+
+    def step():
+        for fp8, bs, rows, cols, codes, scales in mats:
+            capi.moe_requant_fp8_int4(fp8, bs, rows, cols, blk, codes, scales, stream=sh)
+
+    K, W = args.steps, args.warmup
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = hip.event(), hip.event()
+    hip.record(e0, sh, False)
+    for _ in range(K):
+        step()
+    hip.record(e1, sh, False)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(e0, e1) / K
+    # algorithmic bytes: every FP8 byte and block scale read once, codes and
+    # row scales written once
+    nbytes = sum(r * c + bs.numel() * 4 + r * c // 2 + r * 4 for _, bs, r, c, _, _ in mats)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "FP8 -> int4 expert requantization (GB/s of HBM traffic)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"FP8 E4M3 with {blk}x{blk} block scales -> int4 per-row, "
+                               f"{NE} GLM experts (gate/up {2 * I}x{H}, down {H}x{I})",
+                   "experts_per_step": NE},
+        "roofline": {"kernel": "moe::k_requant_fp8_int4", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_step": int(nbytes)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -215,13 +273,16 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="c2",
-                    choices=["c2", "c2i8", "c4i4", "c4i2", "c3", "c1", "c0"])
+                    choices=["c2", "c2i8", "c4i4", "c4i2", "c3", "c1", "c0", "requant"])
     ap.add_argument("--batch", type=int, default=None, help="tokens per step (c4: 2, 4 or 16)")
     ap.add_argument("--layers", type=int, default=8, help="distinct layer instances rotated")
     ap.add_argument("--eager", action="store_true", help="launch each step eagerly (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time every stage")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="adaptive expert top-p (0: off): the router keeps the shortest prefix "
+                         "of each token's top-k whose routing mass reaches this share")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy five times (the known-size kernel "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -236,6 +297,9 @@ def main():
         print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
                           "launches": 5}))
         return
+
+    if args.workload == "requant":
+        return bench_requant(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -252,7 +316,7 @@ def main():
     wl = args.workload
     base = {"c2": "c2", "c2i8": "c2", "c4i4": "c4", "c4i2": "c4", "c3": "c3", "c1": "c1",
             "c0": "c0"}[wl]
-    cfg = gen.get_config(base)
+    cfg = gen.get_config(base, top_p=args.top_p) if args.top_p else gen.get_config(base)
     dtype = {"c4i2": gen.I2, "c2i8": gen.I8}.get(wl, cfg.expert_dtype)
     T = args.batch or (16 if base == "c4" else cfg.batches[0])
     L = args.layers if base in ("c2", "c3", "c4") else 1
@@ -283,11 +347,14 @@ def main():
 
     # ---- unique experts per step (library routing, computed before timing)
     n_active = []
+    kept_slots = []
     for i in range(max(args.steps, 1)):
         l, p = i % L, i % P
         if i < P * L:
             capi.moe_route(desc, layers[l].w_router, layers[l].bias, xs[p], T, idx, tw, ws, nb)
-            n_active.append(len(np.unique(idx.cpu().numpy())))
+            ih = idx.cpu().numpy()
+            n_active.append(len(np.unique(ih[ih >= 0])))
+            kept_slots.append(int((ih >= 0).sum()))
         else:
             n_active.append(n_active[i % (P * L)])
 
@@ -401,7 +468,8 @@ def main():
             "workload": f"{cfg.name}: H={cfg.hidden} I={cfg.inter} E={cfg.n_experts} "
                         f"top-{cfg.top_k} ({'softmax' if cfg.router else 'sigmoid noaux_tc'}) "
                         f"{ {gen.I4: 'int4', gen.I2: 'int2', gen.I8: 'int8', gen.BF16: 'bf16'}[dtype]} experts, "
-                        f"{T} token(s)/step, {L} rotating layer instance(s)",
+                        f"{T} token(s)/step, {L} rotating layer instance(s)"
+                        + (f", adaptive expert top-p {cfg.top_p}" if cfg.top_p else ""),
             "global_batch": T,
             "seq_len": 1,
             "parallelism": "single_gpu",
@@ -409,6 +477,9 @@ def main():
         },
         "layer_hbm_gbps": round(lay_bytes / (ms_step * 1e-3) / 1e9, 1),
         "layer_bytes_per_step": int(lay_bytes),
+        "routing": {"top_p": cfg.top_p,
+                    "experts_per_token": round(float(np.mean(kept_slots)) / T, 3),
+                    "unique_experts_per_step": round(float(np.mean(n_active[:K])), 2)},
         "roofline": roofline,
     }
     if args.stages:

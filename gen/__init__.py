@@ -383,3 +383,23 @@ def host_layer(cfg: Config, layer: int = 0, experts=None, dtype: Optional[int] =
     for e in (range(cfg.n_experts) if experts == "all" else (experts or [])):
         hl.get(e)
     return hl
+
+
+# ---------------------------------------------------------- FP8 inputs --
+
+def fp8_e4m3_matrix(seed: int, rows: int, cols: int, block: int = 128, kind: str = "normal"):
+    """A synthetic FP8 checkpoint matrix: OCP E4M3 bytes [rows][cols] and fp32
+    block scales [ceil(rows/block)][ceil(cols/block)].  kind "normal": weights
+    N(0, 1) rounded to E4M3 (torch's conversion), the shape of a real FP8
+    checkpoint; kind "bytes": every non-NaN byte value, uniformly."""
+    rng = np.random.default_rng([seed, rows, cols, block])
+    if kind == "bytes":
+        b = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        b[(b & 0x7F) == 0x7F] = 0x00
+    else:
+        import torch
+        v = rng.standard_normal((rows, cols)).astype(np.float32)
+        b = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    nb_r, nb_c = -(-rows // block), -(-cols // block)
+    bs = rng.uniform(2.0 ** -12, 2.0 ** -6, size=(nb_r, nb_c)).astype(np.float32)
+    return b, bs

@@ -220,6 +220,22 @@ moe_status moe_dequant_rows(int32_t dtype, const void* codes, const float* scale
                             int32_t row0, int32_t n_rows, float* out_f32,
                             uint16_t* out_bf16_codes, void* stream);
 
+/* FP8 -> int4 requantizer: the step that builds the MOE_I4 container from an
+ * FP8 checkpoint ("colibri" README, "What's implemented": the offline
+ * converter dequantizes 128x128 block scales and requantizes to the engine's
+ * container).  fp8: [rows][cols] OCP E4M3 bytes (no NaN codes; a NaN code
+ * gives an unspecified result for its row), 8-byte aligned; block_scales:
+ * [ceil(rows/block)][ceil(cols/block)] fp32; w = e4m3 * block scale (exact).
+ * Per row: scales[r] = float(m / 7) for m = max |w| (nearest even); codes
+ * [rows][cols/2] (4-byte aligned) = nearest-even(w / scales[r]) clamped to
+ * [-7, 7] (0 where the scale is 0), low nibble first.  cols a multiple of 8,
+ * at most 8192; block a multiple of 8 (else MOE_EUNSUPPORTED).  Matrices
+ * stacked along rows share one call when rows per matrix is a multiple of
+ * block. */
+moe_status moe_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int32_t rows,
+                                int32_t cols, int32_t block, uint8_t* codes, float* scales,
+                                void* stream);
+
 const char* moe_status_str(moe_status s);
 
 #ifdef __cplusplus

@@ -102,6 +102,8 @@ def lib():
             "orc_residual_add": [vp, vp, i64],
             "orc_set_threads": [i32],
             "orc_max_threads": [],
+            "orc_decode_e4m3": [vp, i64, vp],
+            "orc_requant_fp8_int4": [vp, vp, i64, i64, i32, vp, vp],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -323,3 +325,23 @@ def stack_forward_host(layers, x: np.ndarray, eps: float):
         ys.append(y)
         x = residual_add(x, y)
     return x, xs, ys
+
+
+def decode_e4m3(b: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 bytes, as float64."""
+    b = np.ascontiguousarray(b, dtype=np.uint8)
+    out = np.empty(b.shape, dtype=np.float64)
+    _check(lib().orc_decode_e4m3(_p(b), b.size, _p(out)))
+    return out
+
+
+def requant_fp8_int4(fp8: np.ndarray, block_scales: np.ndarray, block: int = 128):
+    """FP8 [rows][cols] with block scales -> (packed int4 codes [rows][cols/2],
+    fp32 per-row scales [rows])."""
+    fp8 = np.ascontiguousarray(fp8, dtype=np.uint8)
+    rows, cols = fp8.shape
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    _check(lib().orc_requant_fp8_int4(_p(fp8), _p(np.ascontiguousarray(block_scales, np.float32)),
+                                      rows, cols, block, _p(codes), _p(scales)))
+    return codes, scales

@@ -56,6 +56,11 @@
  *                        int8 container of int4 codes gives the same bits;
  *                        with top-p, the sum over the kept experts.
  *   orc_rmsnorm          closed-form rms of the output.
+ *   orc_decode_e4m3      every byte against torch's float8_e4m3fn; worked
+ *                        values (0, 2^-9, 2^-6, 1, 448, NaN).
+ *   orc_requant_fp8_int4 exact round trips of integer multiples of a scale;
+ *                        the row's absmax maps to +-7; |q*s - w| <= s/2; ties
+ *                        to even; per-block scales; zero rows.
  *   orc_residual_add     f32 addition, exact cases.
  *
  * Build: gcc -O2 -fopenmp -fno-fast-math -ffp-contract=off -shared -fPIC.
@@ -627,6 +632,65 @@ int orc_layer_forward(const orc_desc* d, const float* w_router, const float* bia
   free(xv);
   free(hb);
   return rc;
+}
+
+/* ------------------------------------------------------- requantizer -- */
+
+/* OCP FP8 E4M3 (the "fn" encoding: no infinities, S.1111.111 is NaN): the
+ * value of a byte from its sign, 4-bit exponent (bias 7) and 3-bit mantissa;
+ * exponent 0 is subnormal, m/8 * 2^-6. */
+static double e4m3_value(uint8_t b) {
+  const int e = (b >> 3) & 0xF, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) v = NAN;
+  else if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(8.0 + (double)m, e - 10);
+  return (b & 0x80) ? -v : v;
+}
+
+int orc_decode_e4m3(const uint8_t* b, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(b[i]);
+  return ORC_OK;
+}
+
+/* The offline FP8 -> int4 converter ("colibri" README, "What's implemented":
+ * FP8 weights with 128x128 block scales are dequantized and requantized to
+ * the engine's per-row int4 container).  The pages fix neither the int4 range
+ * nor the rounding; our reading: w = e4m3(b) * block scale, exact in double;
+ * per row m = max |w|; scale = float(m / 7), nearest even; q = nearest-even
+ * of w / scale, clamped to [-7, 7] (q = 0 where the scale is 0); codes packed
+ * two per byte, low nibble first.  block_scales: [ceil(rows/block)]
+ * [ceil(cols/block)] fp32.  A NaN code is an error (ORC_EINVAL). */
+int orc_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int64_t rows,
+                         int64_t cols, int32_t block, uint8_t* codes, float* scales) {
+  if (rows < 0 || cols <= 0 || (cols & 1) || block <= 0) return ORC_EINVAL;
+  const int64_t bcols = (cols + block - 1) / block;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint8_t* in = fp8 + r * cols;
+    const float* bs = block_scales + (r / block) * bcols;
+    double m = 0.0;
+    for (int64_t c = 0; c < cols; ++c) {
+      const double w = e4m3_value(in[c]) * (double)bs[c / block];
+      if (isnan(w)) bad = 1;
+      if (fabs(w) > m) m = fabs(w);
+    }
+    const float s = (float)(m / 7.0);
+    scales[r] = s;
+    for (int64_t c = 0; c < cols; c += 2) {
+      int q[2];
+      for (int k = 0; k < 2; ++k) {
+        const double w = e4m3_value(in[c + k]) * (double)bs[(c + k) / block];
+        double v = s == 0.0f ? 0.0 : rint(w / (double)s);
+        if (v > 7.0) v = 7.0;
+        if (v < -7.0) v = -7.0;
+        q[k] = (int)v;
+      }
+      codes[r * (cols / 2) + c / 2] = (uint8_t)(((unsigned)q[0] & 0xFu) | (((unsigned)q[1] & 0xFu) << 4));
+    }
+  }
+  return bad ? ORC_EINVAL : ORC_OK;
 }
 
 /* ---------------------------------------------------------------- stack -- */

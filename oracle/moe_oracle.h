@@ -76,4 +76,9 @@ int orc_residual_add(float* x, const double* y, int64_t n);
 void orc_set_threads(int32_t n);
 int32_t orc_max_threads(void);
 
+/* FP8 (OCP E4M3, no infinities) decode, and the FP8 -> int4 requantizer. */
+int orc_decode_e4m3(const uint8_t* b, int64_t n, double* out);
+int orc_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int64_t rows,
+                         int64_t cols, int32_t block, uint8_t* codes, float* scales);
+
 #endif

@@ -81,6 +81,7 @@ def lib():
             "moe_stack_forward": ([D, W, i32, vp, i32, vp, vp, sz, vp], i32),
             "moe_dequant_rows": ([i32, vp, vp, i32, i32, i32, vp, vp, vp], i32),
             "moe_status_str": ([i32], ctypes.c_char_p),
+            "moe_requant_fp8_int4": ([vp, vp, i32, i32, i32, vp, vp, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -242,3 +243,11 @@ def layer_forward(layer, x, out=None, ws: Optional[Workspace] = None, stream=Non
     buf, nbytes = ws.get(moe_workspace_bytes(desc, T))
     moe_layer_forward(desc, make_weights(layer.pointers()), x, T, out, idx, w, buf, nbytes, stream)
     return out, idx, w
+
+
+def moe_requant_fp8_int4(fp8, block_scales, rows: int, cols: int, block: int, codes, scales,
+                         stream=None):
+    """FP8 (E4M3) [rows][cols] + block scales -> packed int4 codes + per-row scales."""
+    _check(lib().moe_requant_fp8_int4(_ptr(fp8), _ptr(block_scales), rows, cols, block,
+                                      _ptr(codes), _ptr(scales), _stream(stream)),
+           "moe_requant_fp8_int4")

@@ -487,6 +487,21 @@ moe_status moe_dequant_rows(int32_t dtype, const void* codes, const float* scale
   return MOE_OK;
 }
 
+moe_status moe_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int32_t rows,
+                                int32_t cols, int32_t block, uint8_t* codes, float* scales,
+                                void* stream) {
+  if (rows < 0 || cols <= 0 || block <= 0) return MOE_EINVAL;
+  if (rows == 0) return MOE_OK;
+  if (!fp8 || !block_scales || !codes || !scales) return MOE_EINVAL;
+  if (!requant_supported(cols, block)) return MOE_EUNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(fp8) & 7) || (reinterpret_cast<uintptr_t>(codes) & 3))
+    return MOE_EINVAL;
+  if (launch_requant_fp8_int4(fp8, block_scales, rows, cols, block, codes, scales,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_EHIP;
+  return MOE_OK;
+}
+
 const char* moe_status_str(moe_status s) {
   switch (s) {
     case MOE_OK: return "MOE_OK";

@@ -178,6 +178,10 @@ hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const 
 hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* topk_w,
                           const float* S, int32_t T, int32_t K, int32_t H, const float* residual,
                           float* out, float* y_copy, hipStream_t s);
+hipError_t launch_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int32_t rows,
+                                   int32_t cols, int32_t block, uint8_t* codes, float* scales,
+                                   hipStream_t s);
+bool requant_supported(int32_t cols, int32_t block);
 hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);

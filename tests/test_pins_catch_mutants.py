@@ -25,6 +25,10 @@ MUTANTS = {
     "topp_no_renormalization": ("    wsum = before;\n", "\n"),
     "topp_one_expert_short": ("while (keep < K && before < thr) before += wk[keep++];", "while (keep < K && before + wk[keep] < thr) before += wk[keep++];"),
     "int8_unsigned": ("return v >= 128 ? v - 256 : v;", "return v;"),
+    "e4m3_exponent_bias": ("else v = ldexp(8.0 + (double)m, e - 10);", "else v = ldexp(8.0 + (double)m, e - 9);"),
+    "requant_round_half_up": ("double v = s == 0.0f ? 0.0 : rint(w / (double)s);", "double v = s == 0.0f ? 0.0 : floor(w / (double)s + 0.5);"),
+    "requant_range_8": ("const float s = (float)(m / 7.0);", "const float s = (float)(m / 8.0);"),
+    "requant_block_transposed": ("const float* bs = block_scales + (r / block) * bcols;", "const float* bs = block_scales + (r % block) * 0;"),
     "sigmoid_sign": ("s[e] = 1.0 / (1.0 + exp(-z[e]));", "s[e] = 1.0 / (1.0 + exp(z[e]));"),
     "silu_sign": ("double h = g / (1.0 + exp(-g)) * u;", "double h = g / (1.0 + exp(g)) * u;"),
     "gate_up_swapped": ("double h = g / (1.0 + exp(-g)) * u;", "double h = u / (1.0 + exp(-u)) * g;"),
