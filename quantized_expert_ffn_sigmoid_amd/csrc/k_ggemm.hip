@@ -130,7 +130,6 @@ __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
 // operand reads of 16 lanes (16 rows, one piece) fall on 16 distinct bank
 // groups.  Two stages: the one the step computes on and the one it fills.
 constexpr int GG_XSTAGE = GG_BM * GG_BK * 2;   // 16 KB
-constexpr int GG_XD = 4;                       // activation register sets in flight
 
 // Workgroup barrier after this wave's LDS writes have completed, without the
 // release fence of __syncthreads (which would also wait for every global load
@@ -140,30 +139,30 @@ __device__ __forceinline__ void gg_barrier() {
 }
 
 // One tile.  WDT: weight format (MOE_I4 or MOE_BF16); DOWN: down projection
-// (else gate/up + SwiGLU); NW: K steps of weights in flight; GUARD: the step
-// count is not a multiple of the unroll (the last group has idle steps).
+// (else gate/up + SwiGLU); GRP: K steps per weight load (int4: 1 or 2; each
+// lane then reads 16 * GRP contiguous bytes of each of its rows); NW: K steps
+// of weights in flight (two groups); XD: activation register sets in flight;
+// GUARD: the step count is not a multiple of the unroll (the last group has
+// idle steps).
 //
 // Streams.  All global loads go to registers, so the compiler tracks each of
 // them and waits for exactly the ones an instruction needs (vector memory
-// completes in issue order).  Activations: the block loads step kt + 1 + GG_XD
+// completes in issue order).  Activations: the block loads step kt + 1 + XD
 // into the register set freed by writing step kt + 1 to the LDS stage that
-// step kt + 1 computes on, so each activation tile has GG_XD steps to arrive.
-// Weights: step kt + NW (or its quad) is loaded into the registers step kt
-// has just consumed.
+// step kt + 1 computes on, so each activation tile has XD steps to arrive.
+// Weights: the group of step kt + NW is loaded into the registers the group
+// of step kt has just consumed.
 //
-// QUAD (int4, K steps a multiple of 4): weights are loaded by quads of 4 K
-// steps, 64 contiguous bytes per lane (4 back-to-back instructions covering
-// 256 contiguous bytes of each row), so that each row is read in runs that
-// keep its DRAM page open; one 16-byte piece of the quad feeds each step.
-// The K order inside a quad follows: step s of quad q takes, for lane group
-// kg, the codes q * 512 + kg * 128 + 32 s + [0, 32), and the activation
-// stages gather the same positions.  NW is then 8 (two quads in flight).
-template <int WDT, bool DOWN, int NW, bool GUARD, bool QUAD>
+// Groups: the K order inside a group follows the loads: step s of group q
+// takes, for lane group kg, the codes q * 128 GRP + kg * 32 GRP + 32 s +
+// [0, 32), and the activation stages gather the same positions.
+template <int WDT, bool DOWN, int GRP, int NW, int XD, bool GUARD>
 __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   constexpr bool I4 = WDT == MOE_I4;
-  static_assert(!QUAD || (I4 && NW == 8), "quads: int4, two in flight");
-  constexpr int U = NW > GG_XD ? NW : GG_XD;   // unroll: whole register rotations
-  static_assert(U % NW == 0 && U % GG_XD == 0, "unroll covers both rotations");
+  static_assert(I4 || GRP == 1, "bf16 weights load one step at a time");
+  static_assert(NW % GRP == 0, "whole groups in flight");
+  constexpr int U = NW > XD ? NW : XD;   // unroll: whole register rotations
+  static_assert(U % NW == 0 && U % XD == 0, "unroll covers both rotations");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15, kg = lane >> 4;
@@ -231,12 +230,11 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
       row = (I4 ? a.x_p : a.x) + (int64_t)tok * K;
     }
-    xsrc[i] = reinterpret_cast<const uint8_t*>(row) +
-              (QUAD ? (xc >> 2) * 256 + (xc & 3) * 16 : 16 * xc);
+    xsrc[i] = reinterpret_cast<const uint8_t*>(row) + (xc >> 2) * (64 * GRP) + (xc & 3) * 16;
   }
   const int nk = K / GG_BK;
   auto load_x = [&](int kt, u32x4g (&v)[4]) {
-    const int64_t off = QUAD ? (int64_t)(kt >> 2) * 1024 + (kt & 3) * 64 : (int64_t)kt * (GG_BK * 2);
+    const int64_t off = (int64_t)(kt / GRP) * (256 * GRP) + (kt % GRP) * 64;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4g*>(xsrc[i] + off);
   };
@@ -245,17 +243,15 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4g*>(lds + buf * GG_XSTAGE + (xrb + 16 * i) * (GG_BK * 2) + xp * 16) = v[i];
   };
-  // weights: per step, int4 16 bytes per N-subtile, bf16 64 bytes; per quad
-  // (QUAD), 64 bytes per N-subtile
-  constexpr int WV = QUAD ? 4 : (I4 ? 1 : 4);
+  // weights: per group and N-subtile, int4 16 * GRP bytes, bf16 64 bytes
+  constexpr int WV = I4 ? GRP : 4;
   auto load_w = [&](int kt, u32x4g (&v)[4][WV]) {
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
       for (int i = 0; i < WV; ++i) {
-        const int64_t off = QUAD ? (int64_t)(kt >> 2) * 256 + kg * 64 + i * 16
-                            : I4 ? (int64_t)kt * 64 + kg * 16
-                                 : (int64_t)kt * 256 + kg * 64 + i * 16;
+        const int64_t off = I4 ? (int64_t)(kt / GRP) * (64 * GRP) + kg * (16 * GRP) + i * 16
+                               : (int64_t)kt * 256 + kg * 64 + i * 16;
         // ordinary (cached) loads: the m-tiles of an expert re-read these
         // rows and find them in L2
         v[ns][i] = *reinterpret_cast<const u32x4g*>(wp[ns] + off);
@@ -268,20 +264,18 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: activation sets of steps 0 .. GG_XD - 1, the first NW weight
-  // steps, step 0 into stage 0 and its register set refilled with step GG_XD
-  constexpr int NWB = QUAD ? NW / 4 : NW;
-  u32x4g xr[GG_XD][4];
+  // prologue: activation sets of steps 0 .. XD - 1, the first NW weight
+  // steps, step 0 into stage 0 and its register set refilled with step XD
+  constexpr int NWB = NW / GRP;   // weight register groups
+  u32x4g xr[XD][4];
   u32x4g wbuf[NWB][4][WV];
 #pragma unroll
-  for (int j = 0; j < GG_XD; ++j) load_x(min(j, nk - 1), xr[j]);
+  for (int j = 0; j < XD; ++j) load_x(min(j, nk - 1), xr[j]);
 #pragma unroll
-  for (int st = 0; st < NW; ++st) {
-    if (!QUAD) load_w(min(st, nk - 1), wbuf[st]);
-    else if ((st & 3) == 3) load_w(min(st, nk - 1), wbuf[st >> 2]);
-  }
+  for (int st = 0; st < NW; ++st)
+    if (st % GRP == GRP - 1) load_w(min(st, nk - 1), wbuf[st / GRP]);
   store_x(0, xr[0]);
-  load_x(min(GG_XD, nk - 1), xr[0]);
+  load_x(min(XD, nk - 1), xr[0]);
   if (threadIdx.x < GG_BM) {
     s_row[threadIdx.x] = meta_row;
     s_rs[threadIdx.x] = meta_rs;
@@ -298,18 +292,18 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       // stage kt & 1 is complete, and every wave is done with stage
       // (kt + 1) & 1, which step kt - 1 computed on
       gg_barrier();
-      store_x((kt + 1) & 1, xr[(st + 1) % GG_XD]);
-      load_x(min(kt + 1 + GG_XD, nk - 1), xr[(st + 1) % GG_XD]);
+      store_x((kt + 1) & 1, xr[(st + 1) % XD]);
+      load_x(min(kt + 1 + XD, nk - 1), xr[(st + 1) % XD]);
       const uint8_t* xs = lds + (kt & 1) * GG_XSTAGE;
       // pin this step's weights here: without it the compiler hoists the
       // conversions of all stages to the top of the group, waiting there for
       // every load in flight
-      const int wsl = QUAD ? ((st >> 2) % NWB) : (st % NW);   // weight stage of this step
+      const int wsl = (st / GRP) % NWB;   // weight group of this step
 #pragma unroll
       for (int ns = 0; ns < 4; ++ns)
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
-          if (!QUAD || i == (st & 3)) asm volatile("" : "+v"(wbuf[wsl][ns][i]));
+          if (!I4 || i == st % GRP) asm volatile("" : "+v"(wbuf[wsl][ns][i]));
         }
       if (!GUARD || kt < nk) {
 #pragma unroll
@@ -323,7 +317,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
           for (int ns = 0; ns < 4; ++ns) {
             bf16x8 bv;
             if constexpr (I4) {
-              const u32x4g wq = wbuf[wsl][ns][QUAD ? (st & 3) : 0];
+              const u32x4g wq = wbuf[wsl][ns][st % GRP];
               const uint32_t w = d == 0 ? wq.x : d == 1 ? wq.y : d == 2 ? wq.z : wq.w;
               bv = as_bf16x8(i4_to_bf16(w, vmask, vone));
             } else {
@@ -335,9 +329,8 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
           }
         }
       }
-      // weight refill: step kt + NW (its quad) into the registers consumed
-      if (!QUAD) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
-      else if ((st & 3) == 3) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
+      // weight refill: the group of step kt + NW into the registers consumed
+      if (st % GRP == GRP - 1) load_w(min(kt + NW, nk - 1), wbuf[wsl]);
     }
   }
 
@@ -372,38 +365,49 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   }
 }
 
-// K steps of weights in flight: eight for int4 weights loaded by quads (64
-// registers per quad), two for int4 K counts that are not a multiple of 4 and
-// for bf16 (64 registers per step); the block runs one wave per SIMD, so the
-// registers are its own.
-constexpr int GG_NW_I4 = 8, GG_NW_BF16 = 2;
-
-template <int WDT, bool DOWN>
-__device__ __forceinline__ void gg_dispatch(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+// int4 tiles run two waves per SIMD (two blocks per CU), so that one wave's
+// int4 unpacking and waits overlap the other's matrix instructions: weights
+// by pairs of K steps, two pairs in flight (64 registers), two activation
+// sets.  bf16 tiles (64 weight registers per step) run one wave per SIMD
+// with two weight steps and four activation sets in flight.
+template <bool DOWN>
+__device__ __forceinline__ void gg_dispatch_i4(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
   const int nk = K / GG_BK;
-  if constexpr (WDT == MOE_I4) {
-    if (nk % 4 == 0) {
-      if (nk % 8 == 0) gg_run<WDT, DOWN, 8, false, true>(a, t, lds);
-      else gg_run<WDT, DOWN, 8, true, true>(a, t, lds);
-      return;
-    }
-    gg_run<WDT, DOWN, 2, true, false>(a, t, lds);   // nk is not a multiple of 4 here
+  if (nk % 2 == 0) {
+    if (nk % 4 == 0) gg_run<MOE_I4, DOWN, 2, 4, 2, false>(a, t, lds);
+    else gg_run<MOE_I4, DOWN, 2, 4, 2, true>(a, t, lds);
   } else {
-    if (nk % 4 == 0) gg_run<WDT, DOWN, GG_NW_BF16, false, false>(a, t, lds);
-    else gg_run<WDT, DOWN, GG_NW_BF16, true, false>(a, t, lds);
+    gg_run<MOE_I4, DOWN, 1, 2, 2, true>(a, t, lds);
   }
 }
 
-template <int WR, int WS, bool DOWN>
-__global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ggemm(GgArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * GG_XSTAGE + 2 * GG_BM * 4];
+template <bool DOWN>
+__device__ __forceinline__ void gg_dispatch_bf16(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+  const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
+  const int nk = K / GG_BK;
+  if (nk % 4 == 0) gg_run<MOE_BF16, DOWN, 1, 2, 4, false>(a, t, lds);
+  else gg_run<MOE_BF16, DOWN, 1, 2, 4, true>(a, t, lds);
+}
+
+constexpr int GG_LDS = 2 * GG_XSTAGE + 2 * GG_BM * 4;
+
+// One launch covers tiles of one weight format: the routed tiles (when
+// max_tiles > 0) and the shared expert's (when has_shared).
+template <bool DOWN>
+__global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ggemm_i4(GgArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_LDS];
   GgTile t;
   if (!gg_tile(a, t)) return;
-  if (t.shared)
-    gg_dispatch<WS, DOWN>(a, t, lds);
-  else
-    gg_dispatch<WR, DOWN>(a, t, lds);
+  gg_dispatch_i4<DOWN>(a, t, lds);
+}
+
+template <bool DOWN>
+__global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_ggemm_bf16(GgArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_LDS];
+  GgTile t;
+  if (!gg_tile(a, t)) return;
+  gg_dispatch_bf16<DOWN>(a, t, lds);
 }
 
 // Tiles of the buckets: active experts in order, ceil(count / 64) tiles each.
@@ -500,29 +504,33 @@ hipError_t launch_make_tiles(const int32_t* offsets, const int32_t* active, cons
 }
 
 hipError_t launch_ggemm(GgArgs a, bool down, int dtype, int shared_dtype, hipStream_t s) {
-  a.nt_r = down ? a.H / 256 : a.I / 128;
-  a.nt_s = a.has_shared ? (down ? a.H / 256 : a.Is / 128) : 0;
-  a.s_tiles = a.has_shared ? (a.T + GG_BM - 1) / GG_BM : 0;
-  if (!a.has_shared) shared_dtype = dtype;
-  const int64_t total = (int64_t)a.max_tiles * a.nt_r + (int64_t)a.s_tiles * a.nt_s;
-  if (total <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
-#define GG_GO(WR, WS, DN) \
-  hipLaunchKernelGGL((k_ggemm<WR, WS, DN>), dim3(blocks), dim3(GG_THREADS), 0, s, a)
-  const bool r4 = dtype == MOE_I4, s4 = shared_dtype == MOE_I4;
-  if (down) {
-    if (r4 && s4) GG_GO(MOE_I4, MOE_I4, true);
-    else if (r4) GG_GO(MOE_I4, MOE_BF16, true);
-    else if (s4) GG_GO(MOE_BF16, MOE_I4, true);
-    else GG_GO(MOE_BF16, MOE_BF16, true);
-  } else {
-    if (r4 && s4) GG_GO(MOE_I4, MOE_I4, false);
-    else if (r4) GG_GO(MOE_I4, MOE_BF16, false);
-    else if (s4) GG_GO(MOE_BF16, MOE_I4, false);
-    else GG_GO(MOE_BF16, MOE_BF16, false);
-  }
-#undef GG_GO
-  return hipGetLastError();
+  // routed tiles and shared tiles of different formats go to separate
+  // launches (the two kernels run at different occupancies)
+  const bool split = a.has_shared && shared_dtype != dtype;
+  auto go = [&](GgArgs q, int wdt) -> hipError_t {
+    q.nt_r = down ? q.H / 256 : q.I / 128;
+    q.nt_s = q.has_shared ? (down ? q.H / 256 : q.Is / 128) : 0;
+    q.s_tiles = q.has_shared ? (q.T + GG_BM - 1) / GG_BM : 0;
+    const int64_t total = (int64_t)q.max_tiles * q.nt_r + (int64_t)q.s_tiles * q.nt_s;
+    if (total <= 0) return hipSuccess;
+    const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    if (wdt == MOE_I4) {
+      if (down) hipLaunchKernelGGL(k_ggemm_i4<true>, dim3(blocks), dim3(GG_THREADS), 0, s, q);
+      else hipLaunchKernelGGL(k_ggemm_i4<false>, dim3(blocks), dim3(GG_THREADS), 0, s, q);
+    } else {
+      if (down) hipLaunchKernelGGL(k_ggemm_bf16<true>, dim3(blocks), dim3(GG_THREADS), 0, s, q);
+      else hipLaunchKernelGGL(k_ggemm_bf16<false>, dim3(blocks), dim3(GG_THREADS), 0, s, q);
+    }
+    return hipGetLastError();
+  };
+  if (!split) return go(a, dtype);
+  GgArgs r = a;
+  r.has_shared = 0;
+  hipError_t st = go(r, dtype);
+  if (st != hipSuccess) return st;
+  GgArgs sh = a;
+  sh.max_tiles = 0;   // shared tiles only
+  return go(sh, shared_dtype);
 }
 
 }  // namespace moe
