@@ -121,14 +121,18 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const float* __restrict__ W
 }
 
 // Prefill shape: 64 tokens x 64 experts per block, fp64 FMA on LDS tiles.
+// With split K (gridDim.z chunks of kc), chunk c writes its partial sums to
+// z + c * T * E and k_logits_reduce adds the chunks in order.
 constexpr int LG_BT = 64, LG_BE = 64, LG_BK = 16;
 __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W,
                                                      const void* __restrict__ x, int act_bf16,
-                                                     int32_t T, int32_t H, int32_t E,
+                                                     int32_t T, int32_t H, int32_t E, int32_t kc,
                                                      double* __restrict__ z) {
   __shared__ float sx[LG_BK][LG_BT + 4];
   __shared__ float sw[LG_BK][LG_BE + 4];
   const int t0 = blockIdx.x * LG_BT, e0 = blockIdx.y * LG_BE;
+  const int kbeg = blockIdx.z * kc, kend = kbeg + kc;
+  z += (int64_t)blockIdx.z * T * E;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   double acc[4][4];
 #pragma unroll
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
   // each thread stages 4 consecutive k of one row of x and of W
   const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;
-  for (int k0 = 0; k0 < H; k0 += LG_BK) {
+  for (int k0 = kbeg; k0 < kend; k0 += LG_BK) {
     {
       const int t = t0 + lr;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -181,9 +185,19 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
   }
 }
 
+// Chunked sums added in chunk order: z = ((p0 + p1) + p2) + ...
+__global__ __launch_bounds__(256) void k_logits_reduce(const double* __restrict__ part, int32_t n_chunks,
+                                                       int64_t n, double* __restrict__ z) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    double v = part[i];
+    for (int c = 1; c < n_chunks; ++c) v += part[(int64_t)c * n + i];
+    z[i] = v;
+  }
+}
+
 hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
                                 int32_t H, int32_t E, double* z, const SliceReq& sr,
-                                hipStream_t s) {
+                                hipStream_t s, double* zpart, int64_t zpart_elems) {
   if (T <= 0) return hipSuccess;
   if (T <= kDecodeTokens) {
     hipLaunchKernelGGL(k_logits_gemv, dim3(E), dim3(256), 0, s, w_router, x, act_bf16, T, H, E,
@@ -194,8 +208,29 @@ hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf
                                               sr.dst_b, s);
       if (st != hipSuccess) return st;
     }
-    dim3 grid((T + LG_BT - 1) / LG_BT, (E + LG_BE - 1) / LG_BE);
-    hipLaunchKernelGGL(k_logits_gemm, grid, dim3(256), 0, s, w_router, x, act_bf16, T, H, E, z);
+    // split K so that the grid fills the chip (about 512 blocks), when a
+    // scratch area for the partial sums is given; H is a multiple of 32
+    const int64_t tiles = (int64_t)((T + LG_BT - 1) / LG_BT) * ((E + LG_BE - 1) / LG_BE);
+    int chunks = 1;
+    if (zpart) {
+      int want = (int)((512 + tiles - 1) / tiles);
+      if (want > 8) want = 8;
+      for (int c = want; c > 1; --c)
+        if ((H / LG_BK) % c == 0 && (int64_t)c * T * E <= zpart_elems) {
+          chunks = c;
+          break;
+        }
+    }
+    dim3 grid((T + LG_BT - 1) / LG_BT, (E + LG_BE - 1) / LG_BE, chunks);
+    hipLaunchKernelGGL(k_logits_gemm, grid, dim3(256), 0, s, w_router, x, act_bf16, T, H, E,
+                       H / chunks, chunks > 1 ? zpart : z);
+    if (chunks > 1) {
+      const int64_t n = (int64_t)T * E;
+      int64_t blocks = (n + 255) / 256;
+      if (blocks > 4096) blocks = 4096;
+      hipLaunchKernelGGL(k_logits_reduce, dim3((unsigned)blocks), dim3(256), 0, s, zpart, chunks,
+                         n, z);
+    }
   }
   return hipGetLastError();
 }

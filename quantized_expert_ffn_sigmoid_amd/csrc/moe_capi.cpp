@@ -203,7 +203,10 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   }
 
   record(opts, MOE_STAGE_ROUTE, 0, s);
-  MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, sr, s));
+  // the partial sums of a split-K router GEMM use the Y area, unused until
+  // the down projections
+  MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, sr, s,
+                               reinterpret_cast<double*>(Y), (int64_t)T * K * H / 2));
   const bool fused_route = T <= kDecodeTokens;
   if (fused_route)
     MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
@@ -342,9 +345,11 @@ moe_status moe_route(const moe_layer_desc* d, const float* w_router, const float
     return MOE_EINVAL;
   if (ws_bytes < moe_workspace_bytes(d, n_tokens)) return MOE_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  double* z = at<double>(ws, carve(*d, n_tokens).z);
+  const Carve c = carve(*d, n_tokens);
+  double* z = at<double>(ws, c.z);
   if (launch_router_logits(w_router, x, d->act_dtype == MOE_BF16, n_tokens, d->hidden,
-                           d->n_experts, z, SliceReq{}, s) != hipSuccess)
+                           d->n_experts, z, SliceReq{}, s, at<double>(ws, c.Y),
+                           (int64_t)n_tokens * d->top_k * d->hidden / 2) != hipSuccess)
     return MOE_EHIP;
   if (launch_router_select(*d, z, bias, n_tokens, topk_idx, topk_w, s) != hipSuccess)
     return MOE_EHIP;

@@ -151,7 +151,7 @@ struct SliceReq {
 // sliced copies that sr asks for (larger T: launch_slice_rows).
 hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
                                 int32_t H, int32_t E, double* z, const SliceReq& sr,
-                                hipStream_t s);
+                                hipStream_t s, double* zpart = nullptr, int64_t zpart_elems = 0);
 // Copies of the T activation rows in the sliced layouts of up to two weight
 // formats (epg 0 or dst null: skipped).
 hipError_t launch_slice_rows(const void* x, int act_bf16, int32_t T, int32_t K, int32_t epg_a,
