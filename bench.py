@@ -146,16 +146,38 @@ def expert_bytes(cfg, dtype):
     return gen.expert_bytes(dtype, cfg.hidden, cfg.inter)
 
 
+def _ring(dtype, K):
+    """Whether the expert GEMV streams rows of length K of this format through
+    its LDS ring (64 lanes on a row, a compiled slice length)."""
+    if dtype == gen.BF16:
+        return K % 512 == 0 and K // 64 in (8, 16, 32, 64, 96)
+    if dtype in (gen.I4, gen.I8):
+        return K % 2048 == 0 and K // 64 in (32, 64, 96)
+    return False
+
+
+def shared_runs_with_router(cfg, dtype, T):
+    """Decode layers with a shared expert run its gate/up and down launches
+    together with the router (its leading blocks compute the logits, then the
+    selection): sigmoid router with at most 256 experts, and ring-streamed
+    rows for both sets.  The gate/up stage then holds the routed experts only."""
+    Is = cfg.inter * max(cfg.n_shared, 1)
+    return (T <= 16 and cfg.n_shared > 0 and cfg.router == gen.SIGMOID_NOAUX_TC
+            and cfg.n_experts <= 256
+            and _ring(dtype, cfg.hidden) and _ring(dtype, cfg.inter)
+            and _ring(cfg.shared_dtype, cfg.hidden) and _ring(cfg.shared_dtype, Is))
+
+
 def gate_up_bytes(cfg, dtype, n_active, T):
-    """Algorithmic bytes of one gate/up launch (routed experts and the shared
-    expert together): every active expert's gate/up codes and scales once,
-    the shared expert's gate/up once, the activations once, h written once."""
+    """Algorithmic bytes of one gate/up launch: every active expert's gate/up
+    codes and scales once, the activations once, h written once; and the
+    shared expert's gate/up once when it shares the launch."""
     eb = expert_bytes(cfg, dtype)
     scale_bytes = 0 if dtype == gen.BF16 else 4 * 2 * cfg.inter
     act = 2 if cfg.act_dtype == gen.BF16 else 4
     b = n_active * (eb["gate_up"] + scale_bytes) + T * cfg.hidden * act
     b += T * cfg.top_k * cfg.inter * act
-    if cfg.n_shared:
+    if cfg.n_shared and not shared_runs_with_router(cfg, dtype, T):
         Is = cfg.inter * cfg.n_shared
         sb = gen.expert_bytes(cfg.shared_dtype, cfg.hidden, Is)
         b += sb["gate_up"] + (0 if cfg.shared_dtype == gen.BF16 else 4 * 2 * Is) + T * Is * act
@@ -442,7 +464,9 @@ def main():
         }
     else:
         roofline = {
-            "kernel": "moe::k_gemv gate/up + SwiGLU (routed and shared experts)",
+            "kernel": ("moe::k_gemv gate/up + SwiGLU (routed experts)"
+                       if shared_runs_with_router(cfg, dtype, T) else
+                       "moe::k_gemv gate/up + SwiGLU (routed and shared experts)"),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,

@@ -26,6 +26,7 @@
 #pragma once
 
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -121,9 +122,8 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       // offset-binary nibbles, even ones in lo's bytes, odd ones in hi's
-      const uint32_t w = gr[d] ^ 0x88888888u;
-      const uint32_t lo = w & 0x0F0F0F0Fu;
-      const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
+      const uint32_t lo = (gr[d] ^ 0x08080808u) & 0x0F0F0F0Fu;
+      const uint32_t hi = ((gr[d] >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
       const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
       const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
       const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -175,22 +175,37 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
   }
 }
 
+// A DPP lane move whose every source lane is valid (quad permutes, mirrors),
+// written so that the compiler folds it into the add that consumes it.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL,
-                                                    0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// a + b over the lane pairs (l, l ^ 16) and (l, l ^ 32): the permlane swaps
+// exchange 16-lane rows (odd rows of one copy with even rows of the other) and
+// 32-lane halves, so the two results hold the pair's two values.
+__device__ __forceinline__ float add_swap16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_swap32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
 // Sum over aligned groups of lpr lanes (a power of two); every lane of a group
-// receives the group's sum.  The first four steps are DPP register moves
-// (quad swaps, then the 8- and 16-lane mirrors), the last two LDS permutes.
+// receives the group's sum.  Quad swaps and the 8- and 16-lane mirrors are DPP
+// operands of the adds; the 32- and 64-lane steps swap rows and halves between
+// registers (no LDS round trip).  Each step adds lane l and its partner in the
+// same pairs, and a + b = b + a, so all lanes hold the same bits.
 __device__ __forceinline__ float group_sum(float v, int lpr) {
   if (lpr >= 2) v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
   if (lpr >= 4) v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
   if (lpr >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
   if (lpr >= 16) v += dpp_f<0x140>(v);  // row_mirror
-  if (lpr >= 32) v += __shfl_xor(v, 16, kWave);
-  if (lpr >= 64) v += __shfl_xor(v, 32, kWave);
+  if (lpr >= 32) v = add_swap16(v);
+  if (lpr >= 64) v = add_swap32(v);
   return v;
 }
 
@@ -404,16 +419,23 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
 constexpr int kRing = 16;
 constexpr int kMaxRingRows = 512;   // rows per block on the ring path
 
-struct RingLds {
+struct __attribute__((aligned(16))) RingLds {
   uint8_t ring[kWaves][kRing][1024];
   float out[2][kMaxRingRows];     // per token of the chunk
   float scale[2][kMaxRingRows];   // gate (or the only matrix), up
 };
 
+// Waits until at most N vector memory loads are outstanding.  The asm form
+// keeps memory accesses from moving across the wait; the builtin repeats it
+// in a form the compiler's own wait insertion sees, so that it does not wait
+// again (for everything) before using registers loaded earlier.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  // gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 at
+  // their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -480,9 +502,12 @@ __device__ __forceinline__ void slices_via_lds(const void* src, const int64_t* x
 // Activation slices read straight from rows in the sliced layout: lane j's
 // piece c of granule g is the 16 bytes at ((g * PPC + c) * 64 + j) * 16, so
 // every load instruction of the wave reads one contiguous 1 KB run.
+// The loads only (bf16 rows stay packed in x's registers until
+// slice_finish), so that the caller can issue more loads before the first
+// use of these.
 template <int EPG, int KSL, int NT, int ABF16>
-__device__ __forceinline__ void slices_sliced(const void* src, const int64_t* xoff, int nt,
-                                              float (&x)[NT][KSL], float (&gs)[NT][KSL / EPG]) {
+__device__ __forceinline__ void slices_sliced_load(const void* src, const int64_t* xoff, int nt,
+                                                   float (&x)[NT][KSL]) {
   constexpr int AB = ABF16 ? 2 : 4, P = 16 / AB, PPC = EPG / P, GPL = KSL / EPG;
   const int j = threadIdx.x & 63;
 #pragma unroll
@@ -490,25 +515,46 @@ __device__ __forceinline__ void slices_sliced(const void* src, const int64_t* xo
     const uint8_t* row = reinterpret_cast<const uint8_t*>(src) + xoff[n < nt ? n : 0] * AB;
 #pragma unroll
     for (int g = 0; g < GPL; ++g) {
-      float s = 0.f;
 #pragma unroll
       for (int c = 0; c < PPC; ++c) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(row + ((int64_t)(g * PPC + c) * 64 + j) * 16);
+        // 16 bytes: 4 floats, or 8 bf16 kept in the first 4 slots of the piece
+        const int b = ABF16 ? g * EPG + c * 8 : g * EPG + c * 4;
+        x[n][b] = __uint_as_float(v.x);
+        x[n][b + 1] = __uint_as_float(v.y);
+        x[n][b + 2] = __uint_as_float(v.z);
+        x[n][b + 3] = __uint_as_float(v.w);
+      }
+    }
+  }
+}
+
+// Widens packed bf16 pieces (bf16 rows) and forms the granule sums.
+template <int EPG, int KSL, int NT, int ABF16>
+__device__ __forceinline__ void slice_finish(float (&x)[NT][KSL], float (&gs)[NT][KSL / EPG]) {
+  constexpr int P = ABF16 ? 8 : 4, PPC = EPG / P, GPL = KSL / EPG;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < PPC; ++c) {
         if constexpr (ABF16) {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          const int b = g * EPG + c * 8;
+          const uint32_t w[4] = {__float_as_uint(x[n][b]), __float_as_uint(x[n][b + 1]),
+                                 __float_as_uint(x[n][b + 2]), __float_as_uint(x[n][b + 3])};
 #pragma unroll
-          for (int d = 0; d < 4; ++d) {
+          for (int d = 3; d >= 0; --d) {
             const float lo = __uint_as_float(w[d] << 16), hi = __uint_as_float(w[d] & 0xFFFF0000u);
-            x[n][g * EPG + c * 8 + 2 * d] = lo;
-            x[n][g * EPG + c * 8 + 2 * d + 1] = hi;
-            s += lo + hi;
+            x[n][b + 2 * d] = lo;
+            x[n][b + 2 * d + 1] = hi;
           }
-        } else {
-          const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                              __uint_as_float(v.w)};
 #pragma unroll
-          for (int d = 0; d < 4; ++d) x[n][g * EPG + c * 4 + d] = f[d];
-          s += (f[0] + f[1]) + (f[2] + f[3]);
+          for (int d = 0; d < 4; ++d) s += x[n][b + 2 * d] + x[n][b + 2 * d + 1];
+        } else {
+          const int b = g * EPG + c * 4;
+          s += (x[n][b] + x[n][b + 1]) + (x[n][b + 2] + x[n][b + 3]);
         }
       }
       gs[n][g] = s;
@@ -516,54 +562,120 @@ __device__ __forceinline__ void slices_sliced(const void* src, const int64_t* xo
   }
 }
 
-// The wave's rows of the block: local rows wave, wave + kWaves, ... < nr.
-// Row results (scaled, SwiGLU applied for PAIR) go to L.out[n][local row].
-// With sliced input rows the weight loads are issued first, so that their
-// latency covers the activation loads and the scale staging; otherwise the
-// activation rows are staged through the ring area before the ring starts.
-// stage_scales: copy the block's row scales to L.scale (first chunk of a
-// block); every wave of the block calls this together.
-template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED>
-__device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff, int nt,
-                         bool stage_scales, RingLds& L) {
-  using F = Fmt<WDT>;
-  constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
-  constexpr int HPG = GB / 16;   // 16-byte slots per granule: 1, or 2 (int8 halves)
-  constexpr int NM = PAIR ? 2 : 1, S = NM * GPL * HPG;
-  static_assert(GB == 16 || (GB == 32 && WDT == MOE_I8), "ring slots hold 16-byte granules or halves");
-  static_assert(WDT != MOE_I8 || (Fmt<MOE_I8>::UNIT == 1.0f / 512.0f && Fmt<MOE_I8>::OFF == 8.0f),
-                "i8_half_fma's constants");
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t rbytes = (int64_t)(jb.K / EPG) * GB;
+// The wave's stream of ring slots over its rows of a block: slot n is local
+// row i = n / S (rows wave, wave + kWaves, ...), matrix m, granule g, half h.
+template <int WDT, int KSL, bool PAIR>
+struct RingStream {
+  static constexpr int EPG = Fmt<WDT>::EPG, GB = Fmt<WDT>::GB, GPL = KSL / EPG;
+  static constexpr int HPG = GB / 16;   // 16-byte slots per granule: 1, or 2 (int8 halves)
+  static constexpr int NM = PAIR ? 2 : 1, S = NM * GPL * HPG;
+  const uint8_t* lane_base;
+  int64_t rbytes;
+  int rows, wave, total;
+  uint8_t* ring;
 
-  float x[NT][KSL], gs[NT][GPL];
-  if constexpr (!SLICED) slices_via_lds<EPG, KSL, NT, ABF16>(src, xoff, nt, jb.K, &L.ring[0][0][0], x, gs);
-
-  const int my_rows = wave < nr ? (nr - wave + kWaves - 1) / kWaves : 0;
-  const int total = my_rows * S;
-  uint8_t* ring = &L.ring[wave][0][0];
-  const uint8_t* lane_base = jb.W + (int64_t)jb.r0 * rbytes + lane * GB;
-  // slot n of the stream: local row i = n / S, matrix m, granule g, half h
-  auto issue = [&](int n) {
+  __device__ __forceinline__ RingStream(const Job& jb, int nr, RingLds& L) {
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    rbytes = (int64_t)(jb.K / EPG) * GB;
+    rows = jb.rows;
+    const int my_rows = wave < nr ? (nr - wave + kWaves - 1) / kWaves : 0;
+    total = my_rows * S;
+    ring = &L.ring[wave][0][0];
+    lane_base = jb.W + (int64_t)jb.r0 * rbytes + lane * GB;
+  }
+  __device__ __forceinline__ const uint8_t* slot_addr(int n) const {
     const int i = n / S, idx = n - i * S;
     const int m = idx / (GPL * HPG), gh = idx - m * (GPL * HPG);
     const int g = gh / HPG, h = gh - g * HPG;
-    const int64_t row = wave + i * kWaves + m * jb.rows;
-    const uint8_t* p = lane_base + row * rbytes + g * (64 * GB) + h * 16;
-    __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(ring + (n & (kRing - 1)) * 1024), 16, 0, 0);
-  };
-  const int pro = total < kRing ? total : kRing;
-  for (int n = 0; n < pro; ++n) issue(n);
-
-  if (stage_scales && WDT != MOE_BF16) {
-    for (int t = threadIdx.x; t < nr; t += kThreads) {
-      L.scale[0][t] = jb.S[jb.r0 + t];
-      if (PAIR) L.scale[1][t] = jb.S[jb.rows + jb.r0 + t];
-    }
-    __syncthreads();
+    const int64_t row = wave + i * kWaves + m * rows;
+    return lane_base + row * rbytes + g * (64 * GB) + h * 16;
   }
-  if constexpr (SLICED) slices_sliced<EPG, KSL, NT, ABF16>(src, xoff, nt, x, gs);
+  __device__ __forceinline__ void issue_at(const uint8_t* p, int n) const {
+    // non-temporal: the codes are read once
+    __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(ring + (n & (kRing - 1)) * 1024), 16, 0, 2);
+  }
+  __device__ __forceinline__ void issue(int n) const { issue_at(slot_addr(n), n); }
+  // Slots [N0, N1) of the ring's first fill; slots past the stream reload the
+  // block's first granule into ring slots that are never read, so that every
+  // wave issues the same loads.
+  template <int N0, int N1>
+  __device__ __forceinline__ void prologue() const {
+#pragma unroll
+    for (int n = N0; n < N1; ++n) issue_at(n < total ? slot_addr(n) : lane_base, n);
+  }
+};
+
+// Ring slots issued before the activation loads.  Register loads and direct
+// LDS loads outstanding together make the compiler wait for all of them
+// before the first use of a loaded register, so the activations are waited
+// for once, early, with only these slots in flight; the rest of the first
+// fill follows.
+constexpr int kRingPre = 4;
+
+// Row scales of a wave's rows (local rows wave, wave + kWaves, ...) into its
+// part of L.scale by direct global-to-LDS loads: no register waits; the ring's
+// first wait covers them, as they are issued before the ring's loads.
+constexpr int kScalePerWave = kMaxRingRows / kWaves;
+__device__ __forceinline__ float* wave_scales(RingLds& L, int m, int wave) {
+  return &L.scale[m][wave * kScalePerWave];
+}
+template <bool PAIR>
+__device__ __forceinline__ void stage_wave_scales(const Job& jb, int nr, int wave, RingLds& L) {
+  const int lane = threadIdx.x & 63;
+  const int my_rows = wave < nr ? (nr - wave + kWaves - 1) / kWaves : 0;
+  for (int c = 0; c < my_rows; c += 64) {
+    const int i = c + lane;
+    const int r = jb.r0 + (i < my_rows ? wave + i * kWaves : 0);
+#pragma unroll
+    for (int m = 0; m < (PAIR ? 2 : 1); ++m)
+      __builtin_amdgcn_global_load_lds(jb.S + m * jb.rows + r, (lds_ptr_t)(wave_scales(L, m, wave) + c),
+                                       4, 0, 0);
+  }
+}
+
+// The wave's rows of the block: local rows wave, wave + kWaves, ... < nr.
+// Row results (scaled, SwiGLU applied for PAIR) go to L.out[n][local row].
+// Activation rows are read sliced, or staged through the ring area before the
+// ring starts; every wave of the block calls this together.
+template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED>
+__device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff, int nt,
+                         RingLds& L) {
+  using F = Fmt<WDT>;
+  using RS = RingStream<WDT, KSL, PAIR>;
+  constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
+  constexpr int HPG = RS::HPG, NM = RS::NM, S = RS::S;
+  static_assert(GB == 16 || (GB == 32 && WDT == MOE_I8), "ring slots hold 16-byte granules or halves");
+  static_assert(WDT != MOE_I8 || (Fmt<MOE_I8>::UNIT == 1.0f / 512.0f && Fmt<MOE_I8>::OFF == 8.0f),
+                "i8_half_fma's constants");
+  static_assert(kMaxRingRows % kWaves == 0, "per-wave scale areas");
+  const int lane = threadIdx.x & 63;
+
+  const RS st(jb, nr, L);
+  const int wave = st.wave, total = st.total, my_rows = total / S;
+  uint8_t* ring = st.ring;
+  // order of the loads: row scales and the first ring slots, the
+  // activations (waited for at once), then the rest of the ring's first fill
+  if constexpr (WDT != MOE_BF16) stage_wave_scales<PAIR>(jb, nr, wave, L);
+  float x[NT][KSL], gs[NT][GPL];
+  if constexpr (!SLICED) {
+    // the ring area stages the activation rows first
+    slices_via_lds<EPG, KSL, NT, ABF16>(src, xoff, nt, jb.K, &L.ring[0][0][0], x, gs);
+    st.template prologue<0, kRing>();
+  } else {
+    st.template prologue<0, kRingPre>();
+    slices_sliced_load<EPG, KSL, NT, ABF16>(src, xoff, nt, x);
+    slice_finish<EPG, KSL, NT, ABF16>(x, gs);
+    // the granule sums are formed (so the activations have landed) before the
+    // rest of the fill is issued
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(gs[n][g]) : : "memory");
+    st.template prologue<kRingPre, kRing>();
+  }
+  const float* sc0 = wave_scales(L, 0, wave);
+  const float* sc1 = wave_scales(L, PAIR ? 1 : 0, wave);
 
   auto read_slot = [&](int n) {
     return *reinterpret_cast<const u32x4*>(ring + (n & (kRing - 1)) * 1024 + lane * 16);
@@ -608,7 +720,7 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
       // the slot has been consumed (its data fed the FMAs above): refill it
 #pragma unroll
       for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(acc[mm][n]) : "v"(v.x), "v"(v.w) : "memory");
-      if (sn + kRing < total) issue(sn + kRing);
+      if (sn + kRing < total) st.issue(sn + kRing);
     }
     const int rl = wave + i * kWaves;
     float red[NM][NT];
@@ -621,8 +733,8 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
       if (n < nt && lane == n) {
         float sa = 1.f, sb = 1.f;
         if constexpr (WDT != MOE_BF16) {
-          sa = L.scale[0][rl] * (1.0f / F::UNIT);
-          if constexpr (PAIR) sb = L.scale[1][rl] * (1.0f / F::UNIT);
+          sa = sc0[i] * (1.0f / F::UNIT);
+          if constexpr (PAIR) sb = sc1[i] * (1.0f / F::UNIT);
         }
         if constexpr (PAIR) {
           const float gv = red[0][n] * sa, uv = red[1][n] * sb;
@@ -633,6 +745,9 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
       }
     }
   }
+  // a wave with fewer rows than the first fill (or none) still has loads in
+  // flight into its ring slots
+  if (total < kRing) wait_vmcnt<0>();
 }
 
 // Which matrix and which token rows a block handles.  Routed and shared
@@ -640,7 +755,9 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
 // of the two (their unpack costs per byte differ).
 struct BlockWork {
   bool shared;
+  bool have_f;   // f0, f1: flat slots of rows 0 and 1 (from the slot tables)
   int e, p0, nrows, rb_index;
+  int f0, f1;    // scalars: an indexed array here would be placed in LDS
 };
 
 // Logical id of block b of n such that the blocks the hardware deals to one
@@ -650,13 +767,15 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t n) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (b >> 3);
 }
 
-__device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
+// b: the block's index among the launch's GEMV blocks.
+__device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw, int64_t b) {
   const int64_t routed_blocks = (int64_t)a.n_slots * a.nb;
   const int64_t shared_blocks = (int64_t)a.nb_s * a.ntg_s;
   const int64_t nblk = routed_blocks + shared_blocks;
   // token mode: the blocks that read the same weight rows for different tokens
   // sit next to each other on one XCD, so the rows come from HBM once
-  const int64_t bid = a.per_token ? xcd_logical(blockIdx.x, nblk) : (int64_t)blockIdx.x;
+  const int64_t bid = a.per_token ? xcd_logical(b, nblk) : b;
+  bw.have_f = false;
   const int64_t before = bid * shared_blocks / nblk;       // shared blocks before bid
   const bool is_shared = (bid + 1) * shared_blocks / nblk > before;
   const RowSource& src = a.src;
@@ -668,7 +787,16 @@ __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
       bw.rb_index = (int)(rbid / a.n_slots);
       bw.p0 = p;
       bw.nrows = 1;
-      if (src.routed) {
+      if (src.routed && src.pos_e) {
+        // the position's expert and flat slot, read together
+        const int e = src.pos_e[p];
+        const int f = src.entries[p];
+        if (e < 0) return false;
+        bw.e = e;
+        bw.f0 = f;
+        bw.f1 = -1;
+        bw.have_f = true;
+      } else if (src.routed) {
         // the active expert whose bucket holds position p (buckets are
         // contiguous and ascending with the active list)
         const int na = *src.n_active;
@@ -688,11 +816,27 @@ __device__ __forceinline__ bool block_work(const GemvArgs& a, BlockWork& bw) {
     }
     const int slot = (int)(rbid / a.nb);
     bw.rb_index = (int)(rbid - (int64_t)slot * a.nb);
-    if (src.routed) {
-      if (slot >= *src.n_active) return false;
-      bw.e = src.active[slot];
-      bw.p0 = src.offsets[bw.e];
-      bw.nrows = src.offsets[bw.e + 1] - bw.p0;
+    if (src.routed && src.slot_tab) {
+      // the slot's whole assignment in one read
+      const int32_t* r = src.slot_tab + (int64_t)slot * kSlotRec;
+      const int4 v = *reinterpret_cast<const int4*>(r);
+      const int f1 = r[4];
+      if (v.x < 0) return false;
+      bw.e = v.x;
+      bw.p0 = v.y;
+      bw.nrows = v.z;
+      bw.f0 = v.w;
+      bw.f1 = f1;
+      bw.have_f = true;
+    } else if (src.routed) {
+      // the active count and the slot's entry in one round trip (slot <
+      // n_slots <= E, so the entry is in bounds even when the slot is idle)
+      const int na = *src.n_active;
+      const int e = src.active[slot];
+      if (slot >= na) return false;
+      bw.e = e;
+      bw.p0 = src.offsets[e];
+      bw.nrows = src.offsets[e + 1] - bw.p0;
     } else {
       bw.e = src.fixed_expert;
       bw.p0 = 0;
@@ -733,7 +877,7 @@ __device__ __forceinline__ Job make_job(const GemvArgs& a, const BlockWork& bw, 
 }
 
 template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN>
-__device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
+__device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
   const Job jb = make_job(a, bw, DOWN);
   if (jb.r0 >= jb.rows) return;
   const RowSource& src = a.src;
@@ -759,13 +903,15 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
     for (int n = 0; n < NTMAX; ++n) {
       const int i = i0 + (n < nt ? n : 0);
       const int q = bw.p0 + i;   // bucket position, fixed-expert row or token
+      // flat slot of a routed row
+      const int f = (!bw.shared && src.routed) ? (bw.have_f ? (i == 0 ? bw.f0 : bw.f1) : src.entries[q]) : 0;
       if (DOWN) {
         xo[n] = (int64_t)q * jb.K;
-        dr[n] = (!bw.shared && src.routed) ? (int64_t)src.entries[q] : (int64_t)q;
+        dr[n] = (!bw.shared && src.routed) ? (int64_t)f : (int64_t)q;
       } else {
         int t;
         if (bw.shared) t = q;
-        else if (src.routed) t = src.entries[q] / src.top_k;
+        else if (src.routed) t = f / src.top_k;
         else t = src.rows ? src.rows[q] / src.row_div : q;
         xo[n] = (int64_t)t * jb.K;
         dr[n] = q;
@@ -773,17 +919,16 @@ __device__ void run_block(const GemvArgs& a, const BlockWork& bw, RingLds& L) {
     }
     if constexpr (kRingFmt) {
       if (ring) {
-        const bool first = i0 == 0;
         if (a.in_sliced) {
           if (NT2 == 2 && nt >= 2)
-            job_ring<WDT, KSL, NT2, ABF16, !DOWN, true>(jb, nr, in, xo, nt, first, L);
+            job_ring<WDT, KSL, NT2, ABF16, !DOWN, true>(jb, nr, in, xo, nt, L);
           else
-            job_ring<WDT, KSL, 1, ABF16, !DOWN, true>(jb, nr, in, xo, 1, first, L);
+            job_ring<WDT, KSL, 1, ABF16, !DOWN, true>(jb, nr, in, xo, 1, L);
         } else {
           if (NT2 == 2 && nt >= 2)
-            job_ring<WDT, KSL, NT2, ABF16, !DOWN, false>(jb, nr, in, xo, nt, first, L);
+            job_ring<WDT, KSL, NT2, ABF16, !DOWN, false>(jb, nr, in, xo, nt, L);
           else
-            job_ring<WDT, KSL, 1, ABF16, !DOWN, false>(jb, nr, in, xo, 1, first, L);
+            job_ring<WDT, KSL, 1, ABF16, !DOWN, false>(jb, nr, in, xo, 1, L);
         }
         __syncthreads();
         const int ntw = (NT2 == 2 && nt >= 2) ? nt : 1;
@@ -819,11 +964,48 @@ template <int WR, int KR, int WS, int KS, int NTMAX, int ABF16, bool DOWN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_gemv(GemvArgs a) {
   __shared__ RingLds lds;
   BlockWork bw;
-  if (!block_work(a, bw)) return;
+  if (!block_work(a, bw, blockIdx.x)) return;
   if (bw.shared)
     run_block<WS, KS, NTMAX, ABF16, DOWN>(a, bw, lds);
   else
     run_block<WR, KR, NTMAX, ABF16, DOWN>(a, bw, lds);
+}
+
+// A shared-expert launch whose first p.blocks blocks run routing work: the
+// router logits of expert row blockIdx.x (gate/up launch) or, in one block,
+// the selection and grouping (down launch).  Their LDS scratch is the ring
+// area, so the launch keeps the GEMV's occupancy.
+static_assert(sizeof(double) * kDecodeTokens * 256 <= sizeof(RingLds::ring), "logits scratch");
+static_assert(sizeof(SelectBucketLds) <= sizeof(RingLds::ring), "selection scratch");
+
+template <int WS, int KS, int ABF16, bool DOWN>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_gemv_pre(
+    GemvArgs a, PreArgs p) {
+  __shared__ RingLds lds;
+  if ((int)blockIdx.x < p.blocks) {
+    if constexpr (!DOWN) {
+      logits_row_block(p.w_router, p.x, p.act_bf16, p.T, p.H, p.E, p.z, p.sr, blockIdx.x,
+                       reinterpret_cast<double*>(&lds.ring[0][0][0]));
+    } else {
+      select_bucket_block<4, true>(p.sp, p.zin, p.bias, p.T, p.idx, p.w, p.counts, p.offsets,
+                                   p.entries, p.inverse, p.active, p.n_active,
+                                   *reinterpret_cast<SelectBucketLds*>(&lds.ring[0][0][0]), p.tb);
+    }
+    return;
+  }
+  BlockWork bw;
+  if (!block_work(a, bw, (int64_t)blockIdx.x - p.blocks)) return;
+  run_block<WS, KS, 1, ABF16, DOWN>(a, bw, lds);
+}
+
+template <int WS, int KS, bool DOWN>
+hipError_t gemv_pre_go(const GemvArgs& a, const PreArgs& p, int act_bf16, unsigned blocks,
+                       hipStream_t s) {
+  if (act_bf16)
+    hipLaunchKernelGGL((k_gemv_pre<WS, KS, 1, DOWN>), dim3(blocks), dim3(kThreads), 0, s, a, p);
+  else
+    hipLaunchKernelGGL((k_gemv_pre<WS, KS, 0, DOWN>), dim3(blocks), dim3(kThreads), 0, s, a, p);
+  return hipGetLastError();
 }
 
 
@@ -853,5 +1035,9 @@ hipError_t gemv_i8_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_i8_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_bf_gu(const GemvArgs&, int, int, int, unsigned, hipStream_t);
 hipError_t gemv_bf_dn(const GemvArgs&, int, int, int, unsigned, hipStream_t);
+// Shared-expert launches with leading routing blocks (shared format, K-slice
+// length a.geo_s.kc).
+hipError_t gemv_pre_gu(const GemvArgs&, const PreArgs&, int, int, unsigned, hipStream_t);
+hipError_t gemv_pre_dn(const GemvArgs&, const PreArgs&, int, int, unsigned, hipStream_t);
 
 }  // namespace moe

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(256) void k_bucket_small(int32_t T, int32_t K, int3
                                                       int32_t* __restrict__ inverse,
                                                       int32_t* __restrict__ active,
                                                       int32_t* __restrict__ n_active) {
-  bucket_small(T, K, E, idx, counts, offsets, entries, inverse, active, n_active);
+  __shared__ BucketSmallLds L;
+  bucket_small(T, K, E, idx, counts, offsets, entries, inverse, active, n_active, L);
 }
 
 hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_idx,

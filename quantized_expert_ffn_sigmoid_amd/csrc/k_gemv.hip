@@ -89,14 +89,18 @@ constexpr int64_t kTargetWaves = 2048;
 constexpr int64_t kTargetBlocks = kTargetWaves / kWaves;
 constexpr int64_t kMinBytesPerWave = 8 * 1024;
 
-hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
-                       int max_rows_per_slot, hipStream_t s) {
+// Fills in the geometry, token mode and block sizes of a launch; returns the
+// number of GEMV blocks (0: no work) or -1 when a shape is not covered.
+// ntmax: tokens one pass of a block takes (1, or 2 where allowed).
+static long long plan_gemv(GemvArgs& a, bool down, int dtype, int& shared_dtype,
+                           int max_rows_per_slot, bool allow_nt2, int& ntmax,
+                           int64_t target_blocks = kTargetBlocks) {
   const int kin = down ? a.I : a.H, kin_s = down ? a.Is : a.H;
   const int rows = down ? a.H : a.I, rows_s = down ? a.H : a.Is;
-  if (!make_geo(dtype, kin, a.geo)) return hipErrorInvalidValue;
+  if (!make_geo(dtype, kin, a.geo)) return -1;
   if (a.has_shared) {
-    if (!make_geo(shared_dtype, kin_s, a.geo_s)) return hipErrorInvalidValue;
-    if (a.geo_s.kc != a.geo.kc || a.geo_s.lpr != a.geo.lpr) return hipErrorInvalidValue;
+    if (!make_geo(shared_dtype, kin_s, a.geo_s)) return -1;
+    if (a.geo_s.kc != a.geo.kc || a.geo_s.lpr != a.geo.lpr) return -1;
   } else {
     a.geo_s = a.geo;
     shared_dtype = dtype;
@@ -106,10 +110,10 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
   // int8 granules, whose registers they would crowd out); buckets that may hold more
   // switch the launch to token mode, which splits them over blocks instead of
   // making one block pass over its rows again
-  const int ntmax = (a.geo.kc <= 32 && dtype != MOE_I8 && max_rows_per_slot >= 2) ? 2 : 1;
+  ntmax = (allow_nt2 && a.geo.kc <= 32 && dtype != MOE_I8 && max_rows_per_slot >= 2) ? 2 : 1;
   a.per_token = max_rows_per_slot > ntmax;
   if (a.per_token) {
-    a.n_slots = a.src.routed ? a.n_tok * a.src.top_k : a.src.n_rows;
+    a.n_slots = a.n_slots == 0 ? 0 : a.src.routed ? a.n_tok * a.src.top_k : a.src.n_rows;
     a.tok_s = ntmax;
     a.ntg_s = (a.n_tok + ntmax - 1) / ntmax;
   } else {
@@ -120,26 +124,35 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
   // the time a byte of each format takes, split evenly over the waves of one
   // resident round; blocks whose rows are rounded up must not spill into a
   // second round, so grow the share until they fit
+  const int act_bf16 = 0;
   const int64_t mat = row_bytes_of(dtype, kin, !down) * rows;
   const int64_t mat_s = a.has_shared ? row_bytes_of(shared_dtype, kin_s, !down) * rows_s : 0;
   const int64_t c_r = cost_per_byte(dtype, act_bf16), c_s = cost_per_byte(shared_dtype, act_bf16);
   int64_t per_wave = ((int64_t)a.n_slots * mat * c_r + (int64_t)a.ntg_s * mat_s * c_s) /
-                     kTargetWaves;
+                     (target_blocks * kWaves);
   if (per_wave < kMinBytesPerWave * c_r) per_wave = kMinBytesPerWave * c_r;
   int nb_s = 0;
   long long blocks = 0;
-  // (nb_s is kept in a.nb_s for the kernel's block mapping)
   for (int it = 0; it < 64; ++it) {
     a.rb = rows_per_block(a.geo, dtype, kin, rows, !down, per_wave / c_r);
     a.nb = (rows + a.rb - 1) / a.rb;
     a.rb_s = a.has_shared ? rows_per_block(a.geo_s, shared_dtype, kin_s, rows_s, !down, per_wave / c_s) : 1;
     nb_s = a.has_shared ? (rows_s + a.rb_s - 1) / a.rb_s : 0;
     blocks = (long long)a.n_slots * a.nb + (long long)nb_s * a.ntg_s;
-    if (blocks <= kTargetBlocks) break;
+    if (blocks <= target_blocks) break;
     per_wave += per_wave / 16 + 1;
   }
   a.nb_s = nb_s;
-  if (blocks <= 0 || max_rows_per_slot <= 0) return hipSuccess;
+  if (blocks <= 0 || max_rows_per_slot <= 0) return 0;
+  return blocks;
+}
+
+hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
+                       int max_rows_per_slot, hipStream_t s) {
+  int ntmax = 1;
+  const long long blocks = plan_gemv(a, down, dtype, shared_dtype, max_rows_per_slot, true, ntmax);
+  if (blocks < 0) return hipErrorInvalidValue;
+  if (blocks == 0) return hipSuccess;
   const unsigned nblk = (unsigned)blocks;
   switch (dtype) {
     case MOE_I4: return (down ? gemv_i4_dn : gemv_i4_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
@@ -148,6 +161,30 @@ hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int a
     case MOE_BF16: return (down ? gemv_bf_dn : gemv_bf_gu)(a, shared_dtype, ntmax, act_bf16, nblk, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemv_pre(GemvArgs a, const PreArgs& p, bool down, int shared_dtype,
+                           int act_bf16, hipStream_t s) {
+  if (!a.has_shared || p.blocks <= 0) return hipErrorInvalidValue;
+  a.n_slots = 0;
+  int ntmax = 1;
+  int sd = shared_dtype;
+  // the routing blocks hold resident slots of their own (each block takes the
+  // kernel's LDS): the shared blocks are sized so that all of them are
+  // resident beside the routing blocks, with at least one per CU
+  int64_t target = kTargetBlocks - p.blocks;
+  if (target < kTargetBlocks / 2) target = kTargetBlocks / 2;
+  const long long blocks = plan_gemv(a, down, shared_dtype, sd, a.n_tok, false, ntmax, target);
+  if (blocks < 0 || !(a.geo_s.lpr == 64)) return hipErrorInvalidValue;
+  const unsigned nblk = (unsigned)(blocks + p.blocks);
+  return (down ? gemv_pre_dn : gemv_pre_gu)(a, p, shared_dtype, act_bf16, nblk, s);
+}
+
+bool gemv_pre_supported(const moe_layer_desc& d, int32_t Is) {
+  if (d.n_shared <= 0 || d.router != MOE_ROUTER_SIGMOID_NOAUX_TC || d.n_experts > 256) return false;
+  const int sd = d.shared_dtype;
+  if (sd != MOE_BF16 && sd != MOE_I4 && sd != MOE_I8) return false;
+  return gemv_ring(sd, d.hidden) && gemv_ring(sd, Is);
 }
 
 }  // namespace moe

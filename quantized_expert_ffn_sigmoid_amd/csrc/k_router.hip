@@ -42,82 +42,14 @@ hipError_t launch_rmsnorm(const float* x, float* out, int32_t T, int32_t H, floa
 
 // ----------------------------------------------------------- router logits
 
-__device__ __forceinline__ float4 load_x4(const void* x, int act_bf16, int64_t off) {
-  if (act_bf16) {
-    uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + off);
-    return make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
-                       bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
-  }
-  return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
-}
-
-// Decode shape (T <= 16): one block of 256 threads per expert row.  Each
-// thread requests its whole slice of the row (up to LG_QT 16-byte quads per
-// pass) before any arithmetic -- branch-free, with clamped addresses -- so a
-// row costs one memory round trip; the tokens then come from L1/L2.  Partial
-// sums are reduced in LDS along a fixed tree (deterministic fp64 order).
-constexpr int LG_QT = 8;
+// Decode shape (T <= 16): one block of 256 threads per expert row
+// (logits_row_block).
 __global__ __launch_bounds__(256) void k_logits_gemv(const float* __restrict__ W,
                                                      const void* __restrict__ x, int act_bf16,
                                                      int32_t T, int32_t H, int32_t E,
                                                      double* __restrict__ z, SliceReq sr) {
   __shared__ double red[kDecodeTokens][256];
-  const int e = blockIdx.x, tid = threadIdx.x;
-  // the blocks also share out the sliced copies of the rows
-  {
-    const int ab = act_bf16 ? 2 : 4;
-    const int64_t pieces = (int64_t)H * ab / 16;
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
-    for (int64_t p = (int64_t)e * 256 + tid; p < pieces; p += (int64_t)E * 256)
-      for (int n = 0; n < T; ++n) {
-        const int64_t row = (int64_t)n * H * ab;
-        if (sr.dst_a && sr.epg_a > 0)
-          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_a) + row, p, sr.epg_a, ab);
-        if (sr.dst_b && sr.epg_b > 0)
-          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_b) + row, p, sr.epg_b, ab);
-      }
-  }
-  const float* wr = W + (int64_t)e * H;
-  const int nq = H / 4;
-  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-  double acc[kDecodeTokens];
-#pragma unroll
-  for (int n = 0; n < kDecodeTokens; ++n) acc[n] = 0.0;
-  for (int q0 = 0; q0 < nq; q0 += 256 * LG_QT) {
-    float4 w[LG_QT];
-#pragma unroll
-    for (int i = 0; i < LG_QT; ++i) {
-      const int q = q0 + tid + 256 * i;
-      const float4 v = *reinterpret_cast<const float4*>(wr + 4 * (q < nq ? q : nq - 1));
-      w[i] = q < nq ? v : zero4;
-    }
-    for (int n = 0; n < T; ++n) {
-      double a = 0.0;
-#pragma unroll
-      for (int i = 0; i < LG_QT; ++i) {
-        const int q = q0 + tid + 256 * i;
-        float4 v = load_x4(x, act_bf16, (int64_t)n * H + 4 * (q < nq ? q : nq - 1));
-        if (q >= nq) v = zero4;
-        a = fma((double)w[i].x, (double)v.x, a);
-        a = fma((double)w[i].y, (double)v.y, a);
-        a = fma((double)w[i].z, (double)v.z, a);
-        a = fma((double)w[i].w, (double)v.w, a);
-      }
-#pragma unroll
-      for (int m = 0; m < kDecodeTokens; ++m)
-        if (m == n) acc[m] += a;
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < kDecodeTokens; ++n)
-    if (n < T) red[n][tid] = acc[n];
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if (tid < st)
-      for (int n = 0; n < T; ++n) red[n][tid] += red[n][tid + st];
-    __syncthreads();
-  }
-  if (tid < T) z[(int64_t)tid * E + e] = red[tid][0];
+  logits_row_block(W, x, act_bf16, T, H, E, z, sr, blockIdx.x, &red[0][0]);
 }
 
 // Prefill shape: 64 tokens x 64 experts per block, fp64 FMA on LDS tiles.
@@ -251,28 +183,19 @@ __global__ __launch_bounds__(256) void k_select(SelectParams p, const double* __
 }
 
 // Decode: selection of all T <= 16 tokens (one wave each) and the grouping,
-// in one block of BK_THREADS threads.
+// in one block (select_bucket_block).
 template <int EPL>
 __global__ __launch_bounds__(256) void k_select_bucket(
     SelectParams p, const double* __restrict__ z, const float* __restrict__ bias, int32_t T,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
-    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
-  __shared__ int32_t s_idx[kDecodeTokens * kMaxTopK];
-  const int nw = blockDim.x >> 6;
-  for (int t = threadIdx.x >> 6; t < T; t += nw) {
-    if (p.softmax)
-      select_token<EPL, true>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
-                              topk_w + (int64_t)t * p.K, s_idx + t * p.K);
-    else
-      select_token<EPL, false>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
-                               topk_w + (int64_t)t * p.K, s_idx + t * p.K);
-  }
-  __syncthreads();
-  bucket_small(T, p.K, p.E, s_idx, counts, offsets, entries, inverse, active, n_active);
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, SlotTables tb) {
+  __shared__ SelectBucketLds L;
+  select_bucket_block<EPL>(p, z, bias, T, topk_idx, topk_w, counts, offsets, entries, inverse,
+                           active, n_active, L, tb);
 }
 
-static SelectParams select_params(const moe_layer_desc& d) {
+SelectParams select_params(const moe_layer_desc& d) {
   SelectParams p;
   p.E = d.n_experts;
   p.K = d.top_k;
@@ -303,13 +226,14 @@ hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const 
 hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const float* bias,
                                 int32_t T, int32_t* topk_idx, float* topk_w, int32_t* counts,
                                 int32_t* offsets, int32_t* entries, int32_t* inverse,
-                                int32_t* active, int32_t* n_active, hipStream_t s) {
+                                int32_t* active, int32_t* n_active, hipStream_t s,
+                                const SlotTables& tb) {
   if (T <= 0 || T > kDecodeTokens) return hipErrorInvalidValue;
   const SelectParams p = select_params(d);
   const int epl = (d.n_experts + 63) / 64;
 #define MOE_SB(N)                                                                            \
   hipLaunchKernelGGL(k_select_bucket<N>, dim3(1), dim3(256), 0, s, p, z, bias, T,            \
-                     topk_idx, topk_w, counts, offsets, entries, inverse, active, n_active)
+                     topk_idx, topk_w, counts, offsets, entries, inverse, active, n_active, tb)
   if (epl <= 1) MOE_SB(1);
   else if (epl <= 2) MOE_SB(2);
   else if (epl <= 4) MOE_SB(4);

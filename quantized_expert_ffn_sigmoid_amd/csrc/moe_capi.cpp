@@ -98,7 +98,7 @@ int32_t epg_of(int32_t dtype) { return dtype == MOE_BF16 ? 8 : 32; }
 // Workspace carve for n tokens.  Every region is 256-byte aligned.
 struct Carve {
   size_t z, idx, w, counts, offsets, entries, inverse, active, n_active, h, h_sh, Y, S, xn, yl,
-      xs, xs_sh, tiles, rs, xp, total;
+      xs, xs_sh, tiles, rs, xp, slot_tab, pos_e, total;
 };
 
 Carve carve(const moe_layer_desc& d, int64_t T) {
@@ -131,6 +131,8 @@ Carve carve(const moe_layer_desc& d, int64_t T) {
   c.tiles = take(sizeof(int32_t) * (5 * (size_t)ggemm_max_tiles((int32_t)T, (int32_t)K, (int32_t)E) + 1));
   c.rs = take(sizeof(float) * (size_t)T * (K + 2));
   c.xp = take(sizeof(uint16_t) * (size_t)T * H);
+  c.slot_tab = take(sizeof(int32_t) * kSlotRec * (size_t)(T * K < E ? T * K : E));
+  c.pos_e = take(sizeof(int32_t) * (size_t)T * K);
   c.total = o;
   return c;
 }
@@ -175,6 +177,13 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   int32_t* inverse = at<int32_t>(ws, c.inverse);
   int32_t* active = at<int32_t>(ws, c.active);
   int32_t* n_active = at<int32_t>(ws, c.n_active);
+  // decode grouping also writes per-slot records for the expert kernels
+  SlotTables tb;
+  if (T <= kDecodeTokens) {
+    tb.slot_tab = at<int32_t>(ws, c.slot_tab);
+    tb.n_tab = T * K < E ? T * K : E;
+    tb.pos_e = at<int32_t>(ws, c.pos_e);
+  }
   void* h = at<void>(ws, c.h);
   void* h_sh = at<void>(ws, c.h_sh);
   float* Y = at<float>(ws, c.Y);
@@ -192,14 +201,98 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
 
   const bool use_gg = T > kDecodeTokens && ggemm_supported(d);
   if (!use_gg && !gemv_layer_ok(d)) return MOE_EUNSUPPORTED;
+  const bool fused_route = T <= kDecodeTokens;
+  // Decode with a shared expert: its launches carry the routing work in their
+  // leading blocks (the shared expert does not depend on the routing), and
+  // the routed launches follow.  The shared gate/up then reads x as it is.
+  const bool pre = !use_gg && fused_route && gu_ring && dn_ring && gemv_pre_supported(d, Ish);
   SliceReq sr{};
   if (gu_ring && !use_gg) {
     sr.epg_a = epg_r;
     sr.dst_a = xs;
-    if (xs_sh != xs) {
+    if (xs_sh != xs && !pre) {
       sr.epg_b = epg_s;
       sr.dst_b = xs_sh;
     }
+  }
+
+  GemvArgs g{};
+  g.w = dev_set(w.routed);
+  if (has_sh) g.ws = dev_set(w.shared);
+  g.src.routed = 1;
+  g.src.active = active;
+  g.src.n_active = n_active;
+  g.src.offsets = offsets;
+  g.src.entries = entries;
+  g.src.slot_tab = tb.slot_tab;
+  g.src.pos_e = tb.pos_e;
+  g.src.top_k = K;
+  g.has_shared = has_sh;
+  g.n_tok = T;
+  g.H = H;
+  g.I = I;
+  g.Is = Ish;
+  g.n_slots = (int64_t)T * K < E ? T * K : E;
+  g.x = gu_ring ? xs : x;
+  g.x_s = gu_ring ? xs_sh : nullptr;
+  g.h = h;
+  g.h_s = h_sh;
+  g.y = Y;
+  g.y_s = S;
+  g.in_sliced = gu_ring;
+  g.out_sliced = gu_ring && dn_ring;
+
+  if (pre) {
+    record(opts, MOE_STAGE_ROUTE, 0, s);
+    GemvArgs gs = g;
+    gs.x = x;
+    gs.x_s = nullptr;
+    gs.in_sliced = 0;
+    PreArgs p{};
+    p.kind = kPreLogits;
+    p.blocks = E;
+    p.w_router = w.w_router;
+    p.x = x;
+    p.act_bf16 = act_bf16;
+    p.T = T;
+    p.H = H;
+    p.E = E;
+    p.z = z;
+    p.sr = sr;
+    MOE_TRY(launch_gemv_pre(gs, p, false, d.shared_dtype, act_bf16, s));
+    gs.in_sliced = g.out_sliced;
+    p = PreArgs{};
+    p.kind = kPreSelect;
+    p.blocks = 1;
+    p.sp = select_params(d);
+    p.T = T;
+    p.zin = z;
+    p.bias = w.bias;
+    p.idx = idx;
+    p.w = tw;
+    p.counts = counts;
+    p.offsets = offsets;
+    p.entries = entries;
+    p.inverse = inverse;
+    p.active = active;
+    p.n_active = n_active;
+    p.tb = tb;
+    MOE_TRY(launch_gemv_pre(gs, p, true, d.shared_dtype, act_bf16, s));
+    record(opts, MOE_STAGE_ROUTE, 1, s);
+    record(opts, MOE_STAGE_BUCKET, 0, s);
+    record(opts, MOE_STAGE_BUCKET, 1, s);
+    g.has_shared = 0;
+    record(opts, MOE_STAGE_GATE_UP, 0, s);
+    MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
+    record(opts, MOE_STAGE_GATE_UP, 1, s);
+    record(opts, MOE_STAGE_DOWN, 0, s);
+    g.in_sliced = g.out_sliced;
+    MOE_TRY(launch_gemv(g, true, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
+    record(opts, MOE_STAGE_DOWN, 1, s);
+    record(opts, MOE_STAGE_COMBINE, 0, s);
+    MOE_TRY(launch_combine(Y, idx, tw, S, T, K, H, residual, out, y_copy, s));
+    record(opts, MOE_STAGE_COMBINE, 1, s);
+    return MOE_OK;
   }
 
   record(opts, MOE_STAGE_ROUTE, 0, s);
@@ -207,10 +300,9 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   // the down projections
   MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, sr, s,
                                reinterpret_cast<double*>(Y), (int64_t)T * K * H / 2));
-  const bool fused_route = T <= kDecodeTokens;
   if (fused_route)
     MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
-                                 active, n_active, s));
+                                 active, n_active, s, tb));
   else
     MOE_TRY(launch_router_select(d, z, w.bias, T, idx, tw, s));
   record(opts, MOE_STAGE_ROUTE, 1, s);
@@ -269,30 +361,6 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     record(opts, MOE_STAGE_COMBINE, 1, s);
     return MOE_OK;
   }
-
-  GemvArgs g{};
-  g.w = dev_set(w.routed);
-  if (d.n_shared > 0) g.ws = dev_set(w.shared);
-  g.src.routed = 1;
-  g.src.active = active;
-  g.src.n_active = n_active;
-  g.src.offsets = offsets;
-  g.src.entries = entries;
-  g.src.top_k = K;
-  g.has_shared = d.n_shared > 0;
-  g.n_tok = T;
-  g.H = H;
-  g.I = I;
-  g.Is = Ish;
-  g.n_slots = (int64_t)T * K < E ? T * K : E;
-  g.x = gu_ring ? xs : x;
-  g.x_s = gu_ring ? xs_sh : nullptr;
-  g.h = h;
-  g.h_s = h_sh;
-  g.y = Y;
-  g.y_s = S;
-  g.in_sliced = gu_ring;
-  g.out_sliced = gu_ring && dn_ring;
 
   record(opts, MOE_STAGE_GATE_UP, 0, s);
   MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));

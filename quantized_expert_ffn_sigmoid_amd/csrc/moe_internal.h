@@ -46,6 +46,19 @@ struct ExpertSetDev {
   int64_t dns_stride;
 };
 
+// Per-slot records written by the decode grouping, so that an expert GEMV
+// block learns its whole assignment from one 32-byte read instead of a chain
+// of dependent lookups.  slot_tab[s * kSlotRec + ...] for active slot s <
+// n_tab: {expert, first bucket position, rows, flat slot of row 0, flat slot
+// of row 1 (or -1)}; expert -1 for s >= n_active.  pos_e[p]: the expert of
+// bucket position p, or -1 for positions past the grouped slots.
+constexpr int kSlotRec = 8;
+struct SlotTables {
+  int32_t* slot_tab = nullptr;
+  int32_t n_tab = 0;
+  int32_t* pos_e = nullptr;
+};
+
 // How a GEMV block finds its expert and rows.
 //  routed: block slot -> expert active[slot] (slots >= n_active exit);
 //          bucket positions p in [offsets[e], offsets[e+1]); slot f = entries[p];
@@ -57,6 +70,8 @@ struct RowSource {
   const int32_t* n_active;
   const int32_t* offsets;
   const int32_t* entries;
+  const int32_t* slot_tab;   // optional (SlotTables), n_slots records
+  const int32_t* pos_e;      // optional (SlotTables)
   int32_t top_k;
   int32_t fixed_expert;
   const int32_t* rows;
@@ -69,6 +84,51 @@ struct RowSource {
 struct MatGeo {
   int32_t kc, lpr, rpp;
 };
+
+// Sliced copies of activation rows for up to two weight formats (epg 0 or
+// dst null: skipped); see GemvArgs for the layout.
+struct SliceReq {
+  int32_t epg_a, epg_b;
+  void* dst_a;
+  void* dst_b;
+};
+
+// Router selection parameters (one layer).
+struct SelectParams {
+  int32_t E, K, G, topk_group, softmax;
+  float scaling;
+  double top_p;   // adaptive expert top-p, active when 0 < top_p < 1
+};
+
+// Routing work that runs in the leading blocks of a shared-expert GEMV launch
+// (decode): the router logits (one block per expert) in the gate/up launch,
+// the selection and grouping (one block) in the down launch.  The shared
+// expert does not depend on the routing, so its weights stream while the
+// router's latency-bound steps run.
+struct PreArgs {
+  int32_t kind;     // kPreLogits or kPreSelect
+  int32_t blocks;   // leading blocks of the launch that run it
+  // router logits
+  const float* w_router;
+  const void* x;
+  int32_t act_bf16, T, H, E;
+  double* z;
+  SliceReq sr;
+  // selection + grouping
+  SelectParams sp;
+  const double* zin;
+  const float* bias;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* entries;
+  int32_t* inverse;
+  int32_t* active;
+  int32_t* n_active;
+  SlotTables tb;
+};
+constexpr int kPreLogits = 1, kPreSelect = 2;
 
 // One GEMV launch: the routed experts of a bucket (or a fixed expert over a
 // row list) and, optionally, the shared expert over tokens 0..n_tok-1.
@@ -140,13 +200,6 @@ struct GgArgs {
 
 hipError_t launch_rmsnorm(const float* x, float* out, int32_t T, int32_t H, float eps,
                           hipStream_t s);
-// Sliced copies of activation rows for up to two weight formats (epg 0 or
-// dst null: skipped); see GemvArgs for the layout.
-struct SliceReq {
-  int32_t epg_a, epg_b;
-  void* dst_a;
-  void* dst_b;
-};
 // Router logits; for T <= kDecodeTokens the same launch also writes the
 // sliced copies that sr asks for (larger T: launch_slice_rows).
 hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf16, int32_t T,
@@ -156,6 +209,7 @@ hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf
 // formats (epg 0 or dst null: skipped).
 hipError_t launch_slice_rows(const void* x, int act_bf16, int32_t T, int32_t K, int32_t epg_a,
                              void* dst_a, int32_t epg_b, void* dst_b, hipStream_t s);
+SelectParams select_params(const moe_layer_desc& d);
 hipError_t launch_router_select(const moe_layer_desc& d, const double* z, const float* bias,
                                 int32_t T, int32_t* topk_idx, float* topk_w, hipStream_t s);
 hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_idx,
@@ -167,12 +221,21 @@ hipError_t launch_bucket(int32_t T, int32_t K, int32_t E, const int32_t* topk_id
 hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
                        int max_rows_per_slot, hipStream_t s);
 bool make_geo(int dtype, int32_t K, MatGeo& g);
+// A shared-expert-only GEMV launch (a.has_shared, no routed slots) whose
+// leading p.blocks blocks run the routing work p (decode).
+hipError_t launch_gemv_pre(GemvArgs a, const PreArgs& p, bool down, int shared_dtype,
+                           int act_bf16, hipStream_t s);
+// Whether launch_gemv_pre covers the layer: sigmoid router with at most 256
+// experts, and a shared set in a format with LDS-ring kernels for its gate/up
+// (input H) and down (input Is) rows.
+bool gemv_pre_supported(const moe_layer_desc& d, int32_t Is);
 // Decode-sized routing: selection for T <= kDecodeTokens tokens and the
 // bucketing, in one single-block launch.
 hipError_t launch_select_bucket(const moe_layer_desc& d, const double* z, const float* bias,
                                 int32_t T, int32_t* topk_idx, float* topk_w, int32_t* counts,
                                 int32_t* offsets, int32_t* entries, int32_t* inverse,
-                                int32_t* active, int32_t* n_active, hipStream_t s);
+                                int32_t* active, int32_t* n_active, hipStream_t s,
+                                const SlotTables& tb = SlotTables{});
 // out[t] = sum_j w[t][j] * Y[t*k + j] + (S ? S[t] : 0) (+ residual[t] when given;
 // then y_copy[t] receives the MoE output without the residual).
 hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* topk_w,

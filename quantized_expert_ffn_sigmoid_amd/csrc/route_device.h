@@ -104,12 +104,6 @@ __device__ __forceinline__ void segment_top2(double& a, double& b, int lpg) {
 // Wave-wide two largest values (a >= b); lanes hold their local (a, b).
 __device__ __forceinline__ void wave_top2(double& a, double& b) { segment_top2(a, b, 64); }
 
-struct SelectParams {
-  int32_t E, K, G, topk_group, softmax;
-  float scaling;
-  double top_p;   // adaptive expert top-p, active when 0 < top_p < 1
-};
-
 // Selection for one token by one wave: zt = the token's E logits; writes its
 // k expert indices and weights (rank order) to idx_out / w_out, and the
 // indices also to idx_lds when given.  Lane l holds experts l*EPL ..
@@ -262,19 +256,32 @@ constexpr int BK_WAVES = BK_THREADS / kWave;
 constexpr int BK_KEY_BITS = 10;   // experts < 1024
 constexpr int BK_SMALL = 512;     // slot counts up to this take the direct path
 
+// LDS scratch of bucket_small (16-byte aligned).
+struct __attribute__((aligned(16))) BucketSmallLds {
+  int key[BK_SMALL];   // expert of the slot or -1 (invalid index, or padding to a multiple of 4)
+  int kf[BK_SMALL];    // 2 * key + (first slot of its expert), or -1
+  int rank[BK_SMALL];
+  int off[kMaxExperts];
+  int cnt[kMaxExperts];
+  int before[kMaxExperts];   // index of the expert in the active list
+  int n_active, n_valid;
+};
+
 // Small slot counts (F <= BK_SMALL): a slot's position is (slots of smaller
 // experts) + (earlier slots of the same expert); every expert counts its
 // slots itself, scanning the slot keys four at a time.  Any block size.
-__device__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx,
-                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                             int32_t* __restrict__ entries, int32_t* __restrict__ inverse,
-                             int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
-  // s_key: expert of the slot or -1 (invalid index, or padding to a multiple
-  // of 4); s_kf: 2 * key + (first slot of its expert), or -1
-  __shared__ __attribute__((aligned(16))) int s_key[BK_SMALL];
-  __shared__ __attribute__((aligned(16))) int s_kf[BK_SMALL];
-  __shared__ int s_rank[BK_SMALL];
-  __shared__ int s_off[kMaxExperts];
+__device__ __forceinline__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx,
+                                             int32_t* __restrict__ counts,
+                                             int32_t* __restrict__ offsets,
+                                             int32_t* __restrict__ entries,
+                                             int32_t* __restrict__ inverse,
+                                             int32_t* __restrict__ active,
+                                             int32_t* __restrict__ n_active, BucketSmallLds& L,
+                                             const SlotTables& tb = SlotTables{}) {
+  int* s_key = L.key;
+  int* s_kf = L.kf;
+  int* s_rank = L.rank;
+  int* s_off = L.off;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int F = T * K, F4 = (F + 3) & ~3;
   for (int f = tid; f < F4; f += nth) {
@@ -311,19 +318,45 @@ __device__ void bucket_small(int32_t T, int32_t K, int32_t E, const int32_t* idx
     counts[e] = cnt;
     offsets[e] = off;
     s_off[e] = off;
-    if (cnt) active[before] = e;
+    L.cnt[e] = cnt;
+    L.before[e] = before;
+    if (cnt) {
+      active[before] = e;
+      if (tb.slot_tab && before < tb.n_tab) {
+        int32_t* r = tb.slot_tab + (int64_t)before * kSlotRec;
+        r[0] = e;
+        r[1] = off;
+        r[2] = cnt;
+      }
+    }
     if (e == E - 1) {
       offsets[E] = off + cnt;
       n_active[0] = before + (cnt ? 1 : 0);
+      L.n_active = before + (cnt ? 1 : 0);
+      L.n_valid = off + cnt;
     }
   }
   __syncthreads();
   for (int f = tid; f < F; f += nth) {
     const int key = s_key[f];
-    const int pos = key < 0 ? -1 : s_off[key] + s_rank[f];
+    const int r = s_rank[f];
+    const int pos = key < 0 ? -1 : s_off[key] + r;
     if (key >= 0) entries[pos] = f;
     inverse[f] = pos;   // -1 for a dropped slot
+    if (key >= 0) {
+      if (tb.pos_e) tb.pos_e[pos] = key;
+      const int b = L.before[key];
+      if (tb.slot_tab && b < tb.n_tab && r < 2) {
+        int32_t* rec = tb.slot_tab + (int64_t)b * kSlotRec;
+        rec[3 + r] = f;
+        if (r == 0 && L.cnt[key] == 1) rec[4] = -1;
+      }
+    }
+    // positions past the grouped slots (dropped ones) hold no expert
+    if (tb.pos_e && f >= L.n_valid) tb.pos_e[f] = -1;
   }
+  if (tb.slot_tab)
+    for (int b = L.n_active + tid; b < tb.n_tab; b += nth) tb.slot_tab[(int64_t)b * kSlotRec] = -1;
 }
 
 __device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx,
@@ -414,6 +447,116 @@ __device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx
     }
     __syncthreads();
   }
+}
+
+// ------------------------------------------------------- decode routing
+__device__ __forceinline__ float4 load_x4(const void* x, int act_bf16, int64_t off) {
+  if (act_bf16) {
+    uint2 b = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(x) + off);
+    return make_float4(bf16_bits_to_f32(b.x & 0xFFFFu), bf16_bits_to_f32(b.x >> 16),
+                       bf16_bits_to_f32(b.y & 0xFFFFu), bf16_bits_to_f32(b.y >> 16));
+  }
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+}
+
+// Router logits of expert row e for T <= 16 tokens, by one block of 256
+// threads; red: LDS scratch of kDecodeTokens * 256 doubles.  Each thread
+// requests its whole slice of the row (up to LG_QT 16-byte quads per pass)
+// before any arithmetic -- branch-free, with clamped addresses -- so a row
+// costs one memory round trip; the tokens then come from L1/L2.  Partial sums
+// are reduced in LDS along a fixed tree (deterministic fp64 order).  The
+// blocks of a launch (one per expert) also share out the sliced copies of the
+// activation rows that sr asks for.
+constexpr int LG_QT = 8;
+__device__ __forceinline__ void logits_row_block(const float* __restrict__ W,
+                                                 const void* __restrict__ x, int act_bf16,
+                                                 int32_t T, int32_t H, int32_t E,
+                                                 double* __restrict__ z, const SliceReq& sr,
+                                                 int e, double* red) {
+  const int tid = threadIdx.x;
+  {
+    const int ab = act_bf16 ? 2 : 4;
+    const int64_t pieces = (int64_t)H * ab / 16;
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    for (int64_t p = (int64_t)e * 256 + tid; p < pieces; p += (int64_t)E * 256)
+      for (int n = 0; n < T; ++n) {
+        const int64_t row = (int64_t)n * H * ab;
+        if (sr.dst_a && sr.epg_a > 0)
+          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_a) + row, p, sr.epg_a, ab);
+        if (sr.dst_b && sr.epg_b > 0)
+          slice_piece(xb + row, reinterpret_cast<uint8_t*>(sr.dst_b) + row, p, sr.epg_b, ab);
+      }
+  }
+  const float* wr = W + (int64_t)e * H;
+  const int nq = H / 4;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  double acc[kDecodeTokens];
+#pragma unroll
+  for (int n = 0; n < kDecodeTokens; ++n) acc[n] = 0.0;
+  for (int q0 = 0; q0 < nq; q0 += 256 * LG_QT) {
+    float4 w[LG_QT];
+#pragma unroll
+    for (int i = 0; i < LG_QT; ++i) {
+      const int q = q0 + tid + 256 * i;
+      const float4 v = *reinterpret_cast<const float4*>(wr + 4 * (q < nq ? q : nq - 1));
+      w[i] = q < nq ? v : zero4;
+    }
+    for (int n = 0; n < T; ++n) {
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < LG_QT; ++i) {
+        const int q = q0 + tid + 256 * i;
+        float4 v = load_x4(x, act_bf16, (int64_t)n * H + 4 * (q < nq ? q : nq - 1));
+        if (q >= nq) v = zero4;
+        a = fma((double)w[i].x, (double)v.x, a);
+        a = fma((double)w[i].y, (double)v.y, a);
+        a = fma((double)w[i].z, (double)v.z, a);
+        a = fma((double)w[i].w, (double)v.w, a);
+      }
+#pragma unroll
+      for (int m = 0; m < kDecodeTokens; ++m)
+        if (m == n) acc[m] += a;
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < kDecodeTokens; ++n)
+    if (n < T) red[n * 256 + tid] = acc[n];
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (tid < st)
+      for (int n = 0; n < T; ++n) red[n * 256 + tid] += red[n * 256 + tid + st];
+    __syncthreads();
+  }
+  if (tid < T) z[(int64_t)tid * E + e] = red[tid * 256];
+}
+
+// LDS scratch of select_bucket_block.
+struct __attribute__((aligned(16))) SelectBucketLds {
+  BucketSmallLds b;
+  int32_t idx[kDecodeTokens * kMaxTopK];
+};
+
+// Selection of all T <= 16 tokens (one wave each) and the grouping of their
+// slots, by one block of 256 threads.  SIGMOID_ONLY: p is a sigmoid router
+// (the softmax variant is not compiled in).
+template <int EPL, bool SIGMOID_ONLY = false>
+__device__ __forceinline__ void select_bucket_block(
+    const SelectParams& p, const double* __restrict__ z, const float* __restrict__ bias,
+    int32_t T, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ entries,
+    int32_t* __restrict__ inverse, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    SelectBucketLds& L, const SlotTables& tb = SlotTables{}) {
+  const int nw = blockDim.x >> 6;
+  for (int t = threadIdx.x >> 6; t < T; t += nw) {
+    if (!SIGMOID_ONLY && p.softmax)
+      select_token<EPL, true>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                              topk_w + (int64_t)t * p.K, L.idx + t * p.K);
+    else
+      select_token<EPL, false>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
+                               topk_w + (int64_t)t * p.K, L.idx + t * p.K);
+  }
+  __syncthreads();
+  bucket_small(T, p.K, p.E, L.idx, counts, offsets, entries, inverse, active, n_active, L.b, tb);
 }
 
 }  // namespace moe
