@@ -79,6 +79,34 @@ __device__ __forceinline__ void wave_argbest(double& v, int& i) {
   i = bi;
 }
 
+// Wave-wide maximum of doubles, returned in every lane: DPP moves within rows
+// of 16 lanes, then swaps of rows and of halves between two copies.
+__device__ __forceinline__ double swap_max(double v, bool halves) {
+  const long long b = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)(b & 0xFFFFFFFFll), hi = (uint32_t)(b >> 32);
+  uint32_t lo2, hi2, lo3, hi3;
+  if (halves) {
+    const auto pl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto ph = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    lo2 = pl[0]; lo3 = pl[1]; hi2 = ph[0]; hi3 = ph[1];
+  } else {
+    const auto pl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto ph = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    lo2 = pl[0]; lo3 = pl[1]; hi2 = ph[0]; hi3 = ph[1];
+  }
+  const double a = __longlong_as_double(((long long)hi2 << 32) | lo2);
+  const double c = __longlong_as_double(((long long)hi3 << 32) | lo3);
+  return fmax(a, c);
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+  v = fmax(v, dpp_d<kDppXor1>(v));
+  v = fmax(v, dpp_d<kDppXor2>(v));
+  v = fmax(v, dpp_d<kDppHalfMirror>(v));
+  v = fmax(v, dpp_d<kDppMirror>(v));
+  v = swap_max(v, false);
+  return swap_max(v, true);
+}
+
 // Two largest values (a >= b) merged with a partner's pair.
 __device__ __forceinline__ void top2_merge(double& a, double& b, double oa, double ob) {
   const double hi = fmax(a, oa), lo = fmin(a, oa);
@@ -197,21 +225,22 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
   int my_idx = 0;
   double my_s = 0.0, my_before = 0.0, ssum = 0.0, z0 = 0.0;
   for (int j = 0; j < p.K; ++j) {
-    // the lane's best: ascending experts, so a strictly larger value wins
-    // and equal values keep the lower index
-    double v = NEG, bs = 0.0;
-    int bi = 0x7FFFFFFF;
+    // the best open value, then the lowest expert holding it (ballots: the
+    // experts of slot i of each lane are i, EPL + i, 2 EPL + i, ...)
+    double m = c[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) m = fmax(m, c[i]);
+    m = wave_max_d(m);
+    int ri = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const bool take = c[i] > v;
-      v = take ? c[i] : v;
-      bi = take ? lane * EPL + i : bi;
-      bs = take ? sv[i] : bs;
+      const uint64_t b = __ballot(c[i] == m);
+      if (b) ri = min(ri, (int)__builtin_ctzll(b) * EPL + i);
     }
-    double rv = v;
-    int ri = bi;
-    wave_argbest(rv, ri);
-    const int owner = min(ri / EPL, kWave - 1);
+    const int owner = min(ri / EPL, kWave - 1), slot = ri % EPL;
+    double bs = sv[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) bs = slot == i ? sv[i] : bs;
     const double s_win = readlane_d(bs, owner);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) c[i] = lane * EPL + i == ri ? NEG : c[i];
