@@ -115,8 +115,8 @@ class Hip:
 # a digest of the sources that build and launch the kernel; once any of them
 # changes the counters no longer describe it and the traffic is reported null.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemv_gate_up__glm_layer_decode_1tok.md")
-TRAFFIC_SOURCES = ["gemv_impl.h", "k_gemv.hip", "k_gemv_i4_gu.hip", "moe_internal.h",
-                   "moe_capi.cpp"]
+TRAFFIC_SOURCES = ["gemv_impl.h", "route_device.h", "k_gemv.hip", "k_gemv_i4_gu.hip",
+                   "moe_internal.h", "moe_capi.cpp"]
 
 
 def kernel_sources_digest() -> str:
