@@ -205,6 +205,37 @@ def test_int8_small_layer(T):
     print(f"  max|err|/rms = {r:.3e}")
 
 
+# Batches past the decode size on formats (or activations) the grouped GEMM
+# does not take: the GEMV kernels in token mode, with the grouping's lookups
+# (no per-slot records at these sizes).
+GEMV_BEYOND_DECODE = [("c0", None, 40, None), ("c0", gen.I8, 33, None), ("c2", gen.I8, 24, [0, 7, 23])]
+
+
+@pytest.mark.parametrize("name,dtype,T,sample", GEMV_BEYOND_DECODE)
+def test_layer_gemv_beyond_decode(name, dtype, T, sample):
+    cfg = gen.get_config(name)
+    if name == "c0" and dtype == gen.I8:
+        cfg = gen.shrink(cfg, expert_dtype=gen.I8, shared_dtype=gen.I8, hidden=128, inter=64,
+                         seed=46)
+    print_case("gemv beyond decode", name, dtype, T)
+    if name == "c0":
+        hl = gen.host_layer(cfg, 0, experts="all")
+        layer = gdev.upload_host_layer(hl, DEV)
+    else:
+        layer = gdev.generate_device_layer(cfg, 0, DEV, dtype=dtype)
+        hl = gen.host_layer(cfg, 0, dtype=dtype)
+    x = gen.x_tokens(cfg, T, batch_id=300 + T)
+    out, idx, w = _layer_gpu(layer, x)
+    ridx, rw, _ = oracle.route(oracle.Desc.from_config(cfg, dtype), hl.w_router, hl.bias, x, T)
+    assert np.array_equal(idx, ridx)
+    assert np.allclose(w, rw, rtol=1e-6, atol=0)
+    rows = np.arange(T) if sample is None else np.array(sample)
+    ref, sidx, _ = oracle.layer_forward_host(hl, np.ascontiguousarray(x[rows]))
+    assert np.array_equal(sidx, ridx[rows])
+    r = assert_close(out[rows], ref, False, f"{name} T={T}")
+    print(f"  max|err|/rms = {r:.3e}")
+
+
 TOPP_LAYER_CASES = [("c2", 1, 0.7), ("c2", 4, 0.5), ("c4", 16, 0.6)]
 
 
