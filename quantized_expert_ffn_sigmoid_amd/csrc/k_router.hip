@@ -60,8 +60,10 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
                                                      const void* __restrict__ x, int act_bf16,
                                                      int32_t T, int32_t H, int32_t E, int32_t kc,
                                                      double* __restrict__ z) {
-  __shared__ float sx[LG_BK][LG_BT + 4];
-  __shared__ float sw[LG_BK][LG_BE + 4];
+  // operands widened to fp64 once, when staged (each is used by 4 threads'
+  // 4 x 4 tiles)
+  __shared__ double sx[LG_BK][LG_BT + 2];
+  __shared__ double sw[LG_BK][LG_BE + 2];
   const int t0 = blockIdx.x * LG_BT, e0 = blockIdx.y * LG_BE;
   const int kbeg = blockIdx.z * kc, kend = kbeg + kc;
   z += (int64_t)blockIdx.z * T * E;
@@ -78,26 +80,26 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
       const int t = t0 + lr;
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (t < T) v = load_x4(x, act_bf16, (int64_t)t * H + k0 + lk);
-      sx[lk + 0][lr] = v.x;
-      sx[lk + 1][lr] = v.y;
-      sx[lk + 2][lr] = v.z;
-      sx[lk + 3][lr] = v.w;
+      sx[lk + 0][lr] = (double)v.x;
+      sx[lk + 1][lr] = (double)v.y;
+      sx[lk + 2][lr] = (double)v.z;
+      sx[lk + 3][lr] = (double)v.w;
       const int e = e0 + lr;
       float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
       if (e < E) w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + k0 + lk);
-      sw[lk + 0][lr] = w.x;
-      sw[lk + 1][lr] = w.y;
-      sw[lk + 2][lr] = w.z;
-      sw[lk + 3][lr] = w.w;
+      sw[lk + 0][lr] = (double)w.x;
+      sw[lk + 1][lr] = (double)w.y;
+      sw[lk + 2][lr] = (double)w.z;
+      sw[lk + 3][lr] = (double)w.w;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < LG_BK; ++k) {
       double a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = (double)sx[k][ty * 4 + i];
+      for (int i = 0; i < 4; ++i) a[i] = sx[k][ty * 4 + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = (double)sw[k][tx * 4 + j];
+      for (int j = 0; j < 4; ++j) b[j] = sw[k][tx * 4 + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
