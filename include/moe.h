@@ -180,11 +180,15 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
  * events[2s] is recorded on `stream` right before the launches of stage s and
  * events[2s+1] right after them.  While the stream is being captured into a
  * graph the records are external event nodes, so each replay times the stage. */
+/* Decode batches (<= 16 tokens) whose shared expert streams through the
+ * GEMV ring (sigmoid router, <= 256 experts) run the shared expert inside the
+ * ROUTE stage: the logits launch also holds its gate/up, the selection launch
+ * its down projection; GATE_UP and DOWN then hold the routed experts only. */
 enum {
   MOE_STAGE_ROUTE = 0,     /* router logits + selection (+ grouping, for <= 16 tokens) */
   MOE_STAGE_BUCKET = 1,    /* batch-union grouping (empty when fused into ROUTE)      */
-  MOE_STAGE_GATE_UP = 2,   /* gate/up + SwiGLU of routed and shared experts, 1 launch */
-  MOE_STAGE_DOWN = 3,      /* down projections of routed and shared experts, 1 launch */
+  MOE_STAGE_GATE_UP = 2,   /* gate/up + SwiGLU of the routed (and shared) experts    */
+  MOE_STAGE_DOWN = 3,      /* down projections of the routed (and shared) experts    */
   MOE_STAGE_COMBINE = 4,   /* weighted combine (+ residual in stacks)                 */
   MOE_N_STAGES = 5
 };
