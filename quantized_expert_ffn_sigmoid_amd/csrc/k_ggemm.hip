@@ -14,7 +14,9 @@
 // the 128 up rows paired with them, so SwiGLU is applied in registers; for down,
 // 256 output rows.  Each of the 4 waves owns 64 weight rows (four 16-row
 // N-subtiles) and all 64 tile rows (four 16-row M-subtiles): 16 accumulator
-// tiles.  The K dimension advances 128 at a time.
+// tiles.  A tile of at most 32 or 16 valid rows (most buckets of a Zipf-shaped
+// routing hold fewer than 64) computes only its first two M-subtiles or its
+// first one.  The K dimension advances 128 at a time.
 //
 // Operands.  Activations (bf16) are staged per K step in LDS, double buffered,
 // rows padded to 272 bytes so that the 16-byte operand reads of 16 lanes fall
@@ -143,7 +145,9 @@ __device__ __forceinline__ void gg_barrier() {
 // lane then reads 16 * GRP contiguous bytes of each of its rows); NW: K steps
 // of weights in flight (two groups); XD: activation register sets in flight;
 // GUARD: the step count is not a multiple of the unroll (the last group has
-// idle steps).
+// idle steps); MS: 16-row M-subtiles computed (tiles of at most 16 or 32 valid
+// rows skip the matrix instructions, activation staging and LDS reads of the
+// rows they do not hold).
 //
 // Streams.  All global loads go to registers, so the compiler tracks each of
 // them and waits for exactly the ones an instruction needs (vector memory
@@ -156,7 +160,7 @@ __device__ __forceinline__ void gg_barrier() {
 // Groups: the K order inside a group follows the loads: step s of group q
 // takes, for lane group kg, the codes q * 128 GRP + kg * 32 GRP + 32 s +
 // [0, 32), and the activation stages gather the same positions.
-template <int WDT, bool DOWN, int GRP, int NW, int XD, bool GUARD>
+template <int WDT, bool DOWN, int GRP, int NW, int XD, bool GUARD, int MS>
 __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   constexpr bool I4 = WDT == MOE_I4;
   static_assert(I4 || GRP == 1, "bf16 weights load one step at a time");
@@ -219,9 +223,9 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // it).
   const int xp = threadIdx.x & 15, xrb = threadIdx.x >> 4;
   const int xc = xp ^ xrb;   // logical piece
-  const uint8_t* xsrc[4];
+  const uint8_t* xsrc[MS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < MS; ++i) {
     const int rr = min(xrb + 16 * i, t.n - 1);
     const uint16_t* row;
     if (DOWN) {
@@ -233,14 +237,14 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
     xsrc[i] = reinterpret_cast<const uint8_t*>(row) + (xc >> 2) * (64 * GRP) + (xc & 3) * 16;
   }
   const int nk = K / GG_BK;
-  auto load_x = [&](int kt, u32x4g (&v)[4]) {
+  auto load_x = [&](int kt, u32x4g (&v)[MS]) {
     const int64_t off = (int64_t)(kt / GRP) * (256 * GRP) + (kt % GRP) * 64;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4g*>(xsrc[i] + off);
+    for (int i = 0; i < MS; ++i) v[i] = *reinterpret_cast<const u32x4g*>(xsrc[i] + off);
   };
-  auto store_x = [&](int buf, const u32x4g (&v)[4]) {
+  auto store_x = [&](int buf, const u32x4g (&v)[MS]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MS; ++i)
       *reinterpret_cast<u32x4g*>(lds + buf * GG_XSTAGE + (xrb + 16 * i) * (GG_BK * 2) + xp * 16) = v[i];
   };
   // weights: per group and N-subtile, int4 16 * GRP bytes, bf16 64 bytes
@@ -258,16 +262,16 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[MS][4];
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms)
+  for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // prologue: activation sets of steps 0 .. XD - 1, the first NW weight
   // steps, step 0 into stage 0 and its register set refilled with step XD
   constexpr int NWB = NW / GRP;   // weight register groups
-  u32x4g xr[XD][4];
+  u32x4g xr[XD][MS];
   u32x4g wbuf[NWB][4][WV];
 #pragma unroll
   for (int j = 0; j < XD; ++j) load_x(min(j, nk - 1), xr[j]);
@@ -308,9 +312,9 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       if (!GUARD || kt < nk) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-          bf16x8 av[4];
+          bf16x8 av[MS];
 #pragma unroll
-          for (int ms = 0; ms < 4; ++ms)
+          for (int ms = 0; ms < MS; ++ms)
             av[ms] = as_bf16x8(*reinterpret_cast<const u32x4g*>(
                 xs + (16 * ms + ln) * (GG_BK * 2) + 16 * ((kg * 4 + d) ^ ln)));
 #pragma unroll
@@ -324,7 +328,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
               bv = as_bf16x8(wbuf[wsl][ns][d]);
             }
 #pragma unroll
-            for (int ms = 0; ms < 4; ++ms)
+            for (int ms = 0; ms < MS; ++ms)
               acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ms], bv, acc[ms][ns], 0, 0, 0);
           }
         }
@@ -339,7 +343,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // down projection reads it (nibble pairs (j, j + 4) within groups of 8).
   const float mul = I4 ? GG_DIV : 1.0f;
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
+  for (int ms = 0; ms < MS; ++ms) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int m = ms * 16 + kg * 4 + j;
@@ -365,6 +369,14 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   }
 }
 
+// The M-subtile count of a tile follows its valid rows.
+template <int WDT, bool DOWN, int GRP, int NW, int XD, bool GUARD>
+__device__ __forceinline__ void gg_run_m(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+  if (t.n > 32) gg_run<WDT, DOWN, GRP, NW, XD, GUARD, 4>(a, t, lds);
+  else if (t.n > 16) gg_run<WDT, DOWN, GRP, NW, XD, GUARD, 2>(a, t, lds);
+  else gg_run<WDT, DOWN, GRP, NW, XD, GUARD, 1>(a, t, lds);
+}
+
 // int4 tiles run two waves per SIMD (two blocks per CU), so that one wave's
 // int4 unpacking and waits overlap the other's matrix instructions: weights
 // by pairs of K steps, two pairs in flight (64 registers), two activation
@@ -375,10 +387,10 @@ __device__ __forceinline__ void gg_dispatch_i4(const GgArgs& a, const GgTile& t,
   const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
   const int nk = K / GG_BK;
   if (nk % 2 == 0) {
-    if (nk % 4 == 0) gg_run<MOE_I4, DOWN, 2, 4, 2, false>(a, t, lds);
-    else gg_run<MOE_I4, DOWN, 2, 4, 2, true>(a, t, lds);
+    if (nk % 4 == 0) gg_run_m<MOE_I4, DOWN, 2, 4, 2, false>(a, t, lds);
+    else gg_run_m<MOE_I4, DOWN, 2, 4, 2, true>(a, t, lds);
   } else {
-    gg_run<MOE_I4, DOWN, 1, 2, 2, true>(a, t, lds);
+    gg_run_m<MOE_I4, DOWN, 1, 2, 2, true>(a, t, lds);
   }
 }
 
@@ -386,8 +398,8 @@ template <bool DOWN>
 __device__ __forceinline__ void gg_dispatch_bf16(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
   const int nk = K / GG_BK;
-  if (nk % 4 == 0) gg_run<MOE_BF16, DOWN, 1, 2, 4, false>(a, t, lds);
-  else gg_run<MOE_BF16, DOWN, 1, 2, 4, true>(a, t, lds);
+  if (nk % 4 == 0) gg_run_m<MOE_BF16, DOWN, 1, 2, 4, false>(a, t, lds);
+  else gg_run_m<MOE_BF16, DOWN, 1, 2, 4, true>(a, t, lds);
 }
 
 constexpr int GG_LDS = 2 * GG_XSTAGE + 2 * GG_BM * 4;
