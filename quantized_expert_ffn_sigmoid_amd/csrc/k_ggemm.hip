@@ -91,6 +91,43 @@ struct GgTile {
 };
 
 __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
+  if (a.nt_r % 8 == 0 && a.nt_s % 8 == 0) {
+    // Blocks are dealt to the 8 XCDs round robin; XCD x takes the n-tiles
+    // nt = x (mod 8) of every m-tile, so each XCD holds the same share of
+    // every expert's work whatever the bucket sizes (contiguous ranges of
+    // tiles would give one XCD the large experts' full tiles).  Order inside
+    // an XCD: expert, n-tile, m-tile, so the m-tiles that use the same
+    // weight rows run together and share them through that XCD's L2.
+    const int x = blockIdx.x % 8;
+    const int64_t j = blockIdx.x / 8;
+    const int R = a.nt_r / 8;
+    const int64_t routed = (int64_t)a.max_tiles * R;
+    if (j < routed) {
+      const int q0 = (int)(j / R);   // an m-tile of the expert whose run holds j
+      if (q0 >= *a.n_tiles) return false;
+      const int first = a.tile_first[q0], cnt = a.tile_cnt[q0];
+      const int64_t rem = j - (int64_t)first * R;
+      const int k = (int)(rem / cnt);
+      const int mt = first + (int)(rem - (int64_t)k * cnt);
+      t.nt = x + 8 * k;
+      t.shared = false;
+      t.e = a.tile_e[mt];
+      t.p0 = a.tile_p0[mt];
+      t.n = a.tile_n[mt];
+    } else {
+      if (a.s_tiles == 0) return false;
+      const int64_t j2 = j - routed;
+      const int k = (int)(j2 / a.s_tiles);
+      if (k >= a.nt_s / 8) return false;
+      const int mt = (int)(j2 - (int64_t)k * a.s_tiles);
+      t.nt = x + 8 * k;
+      t.shared = true;
+      t.e = 0;
+      t.p0 = mt * GG_BM;
+      t.n = min(GG_BM, a.T - t.p0);
+    }
+    return t.n > 0;
+  }
   const int64_t total = (int64_t)a.max_tiles * a.nt_r + (int64_t)a.s_tiles * a.nt_s;
   const int64_t per = (total + 7) / 8;
   // Consecutive logical tiles run on one XCD (blocks are dealt to the 8 XCDs

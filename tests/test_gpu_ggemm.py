@@ -4,7 +4,8 @@ Batches above the decode size with bf16 activations run the expert FFNs as a
 grouped GEMM over 64-row bucket tiles.  These cases compare every output of
 the layer with the oracle on small layers whose buckets span several tiles,
 ragged last tiles and tiles of one row, for int4 and bf16 routed experts and
-int4, bf16 or no shared expert.  The GLM-scale prefill case lives in
+int4, bf16 or no shared expert, with n-tile counts that are and are not
+multiples of 8 (the two tile maps).  The GLM-scale prefill case lives in
 test_gpu_layer.py (sampled tokens).
 """
 import numpy as np
@@ -41,6 +42,13 @@ def _cfg(kind):
     if kind == "i4_odd_k":
         # K steps of 128: 6 (gate/up) and 3 (down), an odd count
         return gen.shrink(base, **dict(small, hidden=768, inter=384, seed=34))
+    if kind == "i4_xcd":
+        # 8 gate/up and 8 down n-tiles: the tile map that gives each XCD the
+        # n-tiles nt = x (mod 8) of every m-tile
+        return gen.shrink(base, **dict(small, hidden=2048, inter=1024, seed=36))
+    if kind == "i4_xcd_i4shared":
+        return gen.shrink(base, **dict(small, hidden=2048, inter=1024, shared_dtype=gen.I4,
+                                       seed=37))
     if kind == "bf16":
         return gen.shrink(base, hidden=256, inter=128, n_experts=8, top_k=2, n_group=2,
                           topk_group=1, expert_dtype=gen.BF16, shared_dtype=gen.BF16,
@@ -50,7 +58,7 @@ def _cfg(kind):
 
 CASES = [("i4_bf16shared", 17), ("i4_bf16shared", 100), ("i4_bf16shared", 300),
          ("i4_i4shared", 70), ("i4_noshared", 65), ("i4_zipf", 400), ("i4_odd_k", 50),
-         ("i4_topp", 120),
+         ("i4_topp", 120), ("i4_xcd", 150), ("i4_xcd_i4shared", 90),
          ("bf16", 40), ("bf16", 129)]
 
 
