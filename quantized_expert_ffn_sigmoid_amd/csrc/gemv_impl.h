@@ -407,7 +407,10 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
 // ------------------------------------------------------------ ring path
 // Rows of at least 64 granules (all 64 lanes of a wave on one row, so every
 // wave load is one contiguous 1 KB run; int8's 32-byte granules take two
-// slots, each a 2 KB run read at every other 16 bytes): the codes stream through a per-wave
+// slots, each a 2 KB run read at every other 16 bytes; int2's 8-byte granules
+// go two 512-byte granule runs to a slot, lanes 0-31 loading the first and
+// lanes 32-63 the second, one load instruction per slot as for the other
+// formats): the codes stream through a per-wave
 // ring of kRing 1 KB LDS slots filled by direct global-to-LDS loads.  Loads
 // in flight then hold no registers, and a slot is refilled as soon as its
 // data has been consumed, so about kRing KB per wave stay in flight.
@@ -562,16 +565,18 @@ __device__ __forceinline__ void slice_finish(float (&x)[NT][KSL], float (&gs)[NT
   }
 }
 
-// The wave's stream of ring slots over its rows of a block: slot n is local
-// row i = n / S (rows wave, wave + kWaves, ...), matrix m, granule g, half h.
+// The wave's stream over its rows of a block: item t is local row
+// i = t / S (rows wave, wave + kWaves, ...), matrix m, granule g, half h; ring
+// slot n holds item n, or items 2n and 2n + 1 (int2).
 template <int WDT, int KSL, bool PAIR>
 struct RingStream {
   static constexpr int EPG = Fmt<WDT>::EPG, GB = Fmt<WDT>::GB, GPL = KSL / EPG;
-  static constexpr int HPG = GB / 16;   // 16-byte slots per granule: 1, or 2 (int8 halves)
+  static constexpr int HPG = GB >= 16 ? GB / 16 : 1;   // 16-byte slots per granule: 1, or 2 (int8 halves)
+  static constexpr int IPS = GB == 8 ? 2 : 1;          // items per slot
   static constexpr int NM = PAIR ? 2 : 1, S = NM * GPL * HPG;
   const uint8_t* lane_base;
   int64_t rbytes;
-  int rows, wave, total;
+  int rows, wave, items, total;   // total: slots
   uint8_t* ring;
 
   __device__ __forceinline__ RingStream(const Job& jb, int nr, RingLds& L) {
@@ -580,16 +585,27 @@ struct RingStream {
     rbytes = (int64_t)(jb.K / EPG) * GB;
     rows = jb.rows;
     const int my_rows = wave < nr ? (nr - wave + kWaves - 1) / kWaves : 0;
-    total = my_rows * S;
+    items = my_rows * S;
+    total = (items + IPS - 1) / IPS;
     ring = &L.ring[wave][0][0];
-    lane_base = jb.W + (int64_t)jb.r0 * rbytes + lane * GB;
+    lane_base = jb.W + (int64_t)jb.r0 * rbytes + (IPS == 2 ? (lane & 31) * 16 : lane * GB);
   }
-  __device__ __forceinline__ const uint8_t* slot_addr(int n) const {
-    const int i = n / S, idx = n - i * S;
+  __device__ __forceinline__ const uint8_t* item_addr(int t) const {
+    const int i = t / S, idx = t - i * S;
     const int m = idx / (GPL * HPG), gh = idx - m * (GPL * HPG);
     const int g = gh / HPG, h = gh - g * HPG;
     const int64_t row = wave + i * kWaves + m * rows;
     return lane_base + row * rbytes + g * (64 * GB) + h * 16;
+  }
+  __device__ __forceinline__ const uint8_t* slot_addr(int n) const {
+    if constexpr (IPS == 1) {
+      return item_addr(n);
+    } else {
+      // an odd item count leaves the last slot's second half reloading the
+      // block's first granule run, never read
+      const int t = 2 * n + ((threadIdx.x >> 5) & 1);
+      return t < items ? item_addr(t) : lane_base;
+    }
   }
   __device__ __forceinline__ void issue_at(const uint8_t* p, int n) const {
     // non-temporal: the codes are read once
@@ -645,14 +661,16 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
   using RS = RingStream<WDT, KSL, PAIR>;
   constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
   constexpr int HPG = RS::HPG, NM = RS::NM, S = RS::S;
-  static_assert(GB == 16 || (GB == 32 && WDT == MOE_I8), "ring slots hold 16-byte granules or halves");
+  static_assert(GB == 16 || (GB == 32 && WDT == MOE_I8) || (GB == 8 && WDT == MOE_I2),
+                "ring slots hold 16-byte granules, halves of int8 ones or pairs of int2 ones");
   static_assert(WDT != MOE_I8 || (Fmt<MOE_I8>::UNIT == 1.0f / 512.0f && Fmt<MOE_I8>::OFF == 8.0f),
                 "i8_half_fma's constants");
   static_assert(kMaxRingRows % kWaves == 0, "per-wave scale areas");
   const int lane = threadIdx.x & 63;
 
+  constexpr int IPS = RS::IPS;
   const RS st(jb, nr, L);
-  const int wave = st.wave, total = st.total, my_rows = total / S;
+  const int wave = st.wave, total = st.total, my_rows = st.items / S;
   uint8_t* ring = st.ring;
   // order of the loads: row scales and the first ring slots, the
   // activations (waited for at once), then the rest of the ring's first fill
@@ -677,17 +695,24 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
   const float* sc0 = wave_scales(L, 0, wave);
   const float* sc1 = wave_scales(L, PAIR ? 1 : 0, wave);
 
-  auto read_slot = [&](int n) {
-    return *reinterpret_cast<const u32x4*>(ring + (n & (kRing - 1)) * 1024 + lane * 16);
+  auto read_item = [&](int t) {
+    if constexpr (IPS == 1) {
+      return *reinterpret_cast<const u32x4*>(ring + (t & (kRing - 1)) * 1024 + lane * 16);
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(ring + ((t >> 1) & (kRing - 1)) * 1024 +
+                                                      (t & 1) * 512 + lane * 8);
+      return u32x4{v.x, v.y, 0u, 0u};
+    }
   };
-  // slot sn + 1 is read while slot sn is computed; before its read, the loads
-  // younger than it are ring refills (and, early on, the activation and scale
-  // loads, which only make the count conservative), at most kRing - 2 of them
+  // item t + 1 is read while item t is computed; before the read of a slot's
+  // first item, the loads younger than that slot are ring refills (and, early
+  // on, the activation and scale loads, which only make the count
+  // conservative), at most kRing - 2 of them
   u32x4 vnext = {0u, 0u, 0u, 0u};
   if (total > 0) {
     if (total - 1 >= kRing - 2) wait_vmcnt<kRing - 2>();
     else wait_vmcnt<0>();
-    vnext = read_slot(0);
+    vnext = read_item(0);
   }
 
   for (int i = 0; i < my_rows; ++i) {
@@ -698,18 +723,26 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
       for (int n = 0; n < NT; ++n) acc[m][n] = 0.f;
 #pragma unroll
     for (int idx = 0; idx < S; ++idx) {
-      const int sn = i * S + idx;
+      const int t = i * S + idx;
+      const int sn = t / IPS;   // the item's slot
       const u32x4 v = vnext;
-      if (sn + 1 < total) {
-        if (total - sn - 2 >= kRing - 2) wait_vmcnt<kRing - 2>();
-        else wait_vmcnt<0>();
-        vnext = read_slot(sn + 1);
+      if (t + 1 < st.items) {
+        if ((t + 1) % IPS == 0) {
+          if (total - sn - 2 >= kRing - 2) wait_vmcnt<kRing - 2>();
+          else wait_vmcnt<0>();
+        }
+        vnext = read_item(t + 1);
       }
-      const uint32_t gr[4] = {v.x, v.y, v.z, v.w};
       const int mm = idx / (GPL * HPG), gh = idx % (GPL * HPG);
       const int g = gh / HPG, h = gh % HPG;
-      if constexpr (HPG == 1) granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
-      else i8_half_fma<NT, KSL>(gr, x, g * EPG + 16 * h, acc[mm]);
+      if constexpr (IPS == 2) {
+        const uint32_t gr[2] = {v.x, v.y};
+        granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
+      } else {
+        const uint32_t gr[4] = {v.x, v.y, v.z, v.w};
+        if constexpr (HPG == 1) granule_fma<WDT, NT, KSL>(gr, x, g, acc[mm]);
+        else i8_half_fma<NT, KSL>(gr, x, g * EPG + 16 * h, acc[mm]);
+      }
       if constexpr (WDT != MOE_BF16) {
         // the offset after the granule's last slot
         if (h == HPG - 1) {
@@ -717,10 +750,11 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
           for (int n = 0; n < NT; ++n) acc[mm][n] = fmaf(-F::OFF * F::UNIT, gs[n][g], acc[mm][n]);
         }
       }
-      // the slot has been consumed (its data fed the FMAs above): refill it
+      // after its last item the slot has been consumed (its data fed the
+      // FMAs above): refill it
 #pragma unroll
-      for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(acc[mm][n]) : "v"(v.x), "v"(v.w) : "memory");
-      if (sn + kRing < total) st.issue(sn + kRing);
+      for (int n = 0; n < NT; ++n) asm volatile("" : "+v"(acc[mm][n]) : "v"(v.x), "v"(IPS == 2 ? v.y : v.w) : "memory");
+      if (t % IPS == IPS - 1 && sn + kRing < total) st.issue(sn + kRing);
     }
     const int rl = wave + i * kWaves;
     float red[NM][NT];
@@ -883,12 +917,12 @@ __device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
   const RowSource& src = a.src;
   const void* in = DOWN ? (bw.shared ? a.h_s : a.h) : (bw.shared && a.x_s ? a.x_s : a.x);
   void* out = DOWN ? (void*)(bw.shared ? a.y_s : a.y) : (bw.shared ? a.h_s : a.h);
-  // 16-byte granules (and int8's 32-byte ones, as two slots) on rows of >= 64
-  // granules take the ring path (the launcher keeps blocks within
-  // kMaxRingRows rows); slices longer than one granule only occur on such
-  // rows, so the register path is compiled for one-granule slices and int2
-  // only
-  constexpr bool kRingFmt = Fmt<WDT>::GB == 16 || WDT == MOE_I8;
+  // 16-byte granules (and int8's 32-byte ones, as two slots, and int2's
+  // 8-byte ones, two to a slot) on rows of >= 64 granules take the ring path
+  // (the launcher keeps blocks within kMaxRingRows rows); slices longer than
+  // one granule only occur on such rows, so the register path is compiled
+  // for one-granule slices only
+  constexpr bool kRingFmt = Fmt<WDT>::GB == 16 || WDT == MOE_I8 || WDT == MOE_I2;
   constexpr bool kChunk = !kRingFmt || KSL == Fmt<WDT>::EPG;
   constexpr int EPG = Fmt<WDT>::EPG, AB = ABF16 ? 2 : 4;
   const bool ring = kRingFmt && jb.lpr == 64;

@@ -41,7 +41,8 @@ bool gemv_supported(int dtype, int32_t K) {
 
 bool gemv_ring(int dtype, int32_t K) {
   MatGeo g;
-  return (dtype == MOE_I4 || dtype == MOE_I8 || dtype == MOE_BF16) && make_geo(dtype, K, g) &&
+  return (dtype == MOE_I4 || dtype == MOE_I2 || dtype == MOE_I8 || dtype == MOE_BF16) &&
+         make_geo(dtype, K, g) &&
          g.lpr == 64;
 }
 

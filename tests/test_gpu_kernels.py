@@ -239,6 +239,8 @@ FFN_CASES = [
     ("c2", gen.I4, False, 200, 5, True),
     ("c2", gen.I4, True, 0, 2, False),
     ("c4", gen.I2, False, 9, 4, True),
+    ("c4", gen.I2, False, 70, 1, False),
+    ("c2", gen.I2, False, 5, 2, False),
     ("c0", gen.I8, False, 5, 3, False),
     ("c2", gen.I8, False, 33, 1, False),
     ("c2", gen.I8, False, 150, 6, True),

@@ -43,7 +43,7 @@ def _oracle_layer(cfg, layer_idx, x, dtype=None, tokens=None):
 LAYER_CASES = [("c0", None, 1), ("c0", None, 3), ("c0", None, 7), ("c2", None, 1),
                ("c2", gen.I8, 1), ("c2", gen.I8, 5),
                ("c2", None, 16), ("c4", gen.I4, 2), ("c4", gen.I2, 4), ("c4", gen.I4, 16),
-               ("c4", gen.I2, 16),
+               ("c4", gen.I2, 16), ("c4", gen.I2, 1), ("c4", gen.I2, 2), ("c2", gen.I2, 3),
                ("c1", None, 1), ("c1", None, 16)]
 
 
