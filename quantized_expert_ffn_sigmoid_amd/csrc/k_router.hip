@@ -73,26 +73,30 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-  // each thread stages 4 consecutive k of one row of x and of W
+  // each thread stages 4 consecutive k of one row of x and of W; the next
+  // step's values are loaded into registers while the current step computes
   const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;
+  const int t = t0 + lr, e = e0 + lr;
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto load = [&](int k0) {
+    if (t < T) v = load_x4(x, act_bf16, (int64_t)t * H + k0 + lk);
+    if (e < E) w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + k0 + lk);
+  };
+  // workgroup barrier after this wave's LDS accesses, without the release
+  // fence of __syncthreads (which would also wait for the loads in flight)
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+  if (kbeg < kend) load(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += LG_BK) {
-    {
-      const int t = t0 + lr;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < T) v = load_x4(x, act_bf16, (int64_t)t * H + k0 + lk);
-      sx[lk + 0][lr] = (double)v.x;
-      sx[lk + 1][lr] = (double)v.y;
-      sx[lk + 2][lr] = (double)v.z;
-      sx[lk + 3][lr] = (double)v.w;
-      const int e = e0 + lr;
-      float4 w = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (e < E) w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + k0 + lk);
-      sw[lk + 0][lr] = (double)w.x;
-      sw[lk + 1][lr] = (double)w.y;
-      sw[lk + 2][lr] = (double)w.z;
-      sw[lk + 3][lr] = (double)w.w;
-    }
-    __syncthreads();
+    sx[lk + 0][lr] = (double)v.x;
+    sx[lk + 1][lr] = (double)v.y;
+    sx[lk + 2][lr] = (double)v.z;
+    sx[lk + 3][lr] = (double)v.w;
+    sw[lk + 0][lr] = (double)w.x;
+    sw[lk + 1][lr] = (double)w.y;
+    sw[lk + 2][lr] = (double)w.z;
+    sw[lk + 3][lr] = (double)w.w;
+    lds_barrier();
+    if (k0 + LG_BK < kend) load(k0 + LG_BK);
 #pragma unroll
     for (int k = 0; k < LG_BK; ++k) {
       double a[4], b[4];
@@ -105,7 +109,7 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
     }
-    __syncthreads();
+    lds_barrier();
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -142,12 +146,12 @@ hipError_t launch_router_logits(const float* w_router, const void* x, int act_bf
                                               sr.dst_b, s);
       if (st != hipSuccess) return st;
     }
-    // split K so that the grid fills the chip (about 512 blocks), when a
+    // split K so that the grid fills the chip (about 1024 blocks), when a
     // scratch area for the partial sums is given; H is a multiple of 32
     const int64_t tiles = (int64_t)((T + LG_BT - 1) / LG_BT) * ((E + LG_BE - 1) / LG_BE);
     int chunks = 1;
     if (zpart) {
-      int want = (int)((512 + tiles - 1) / tiles);
+      int want = (int)((1024 + tiles - 1) / tiles);
       if (want > 8) want = 8;
       for (int c = want; c > 1; --c)
         if ((H / LG_BK) % c == 0 && (int64_t)c * T * E <= zpart_elems) {
