@@ -437,9 +437,10 @@ def main():
     for k, s_id in enumerate(stage_ids):
         stage_ms[s_id] = [hip.elapsed_ms(evs[i][k][0], evs[i][k][1]) for i in range(K)]
     # the event bracket holds the kernel plus the event nodes' own latency,
-    # which an empty event pair in the same replay measures
-    bracket_ms = float(np.mean(stage_ms[capi.MOE_STAGE_GATE_UP]))
-    pair_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in evp]))
+    # which an empty event pair in the same replay measures; medians over the
+    # steps, as a few pairs now and then take several times their usual time
+    bracket_ms = float(np.median(stage_ms[capi.MOE_STAGE_GATE_UP]))
+    pair_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evp]))
     gu_ms = bracket_ms - pair_ms if bracket_ms > 2 * pair_ms else bracket_ms
     gu_bytes = float(np.mean([gate_up_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     lay_bytes = float(np.mean([layer_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
