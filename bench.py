@@ -15,9 +15,11 @@ from the 256 MB Infinity Cache, as successive layers of a decoder would.
 The timed steps are captured once into a HIP graph and replayed (the library
 allocates nothing and never synchronises, so the whole step is capturable).
 A second replay of the same steps carries an event pair around the gate/up
-launch of every step (and around every stage with --stages), and an empty
-event pair whose latency is subtracted from the bracket: it times the
-dominant kernel without putting event nodes into the headline loop.
+launch of every step (and around every stage with --stages), and a third an
+event pair around every whole step: its median less the event-free time per
+step is what a bracket adds around running kernels, and is subtracted from
+the gate/up bracket.  This times the dominant kernel without putting event
+nodes into the headline loop.
 
 Output: one JSON line (see the fields below).  --gpus N > 1 exits: this
 build runs on one GPU.
@@ -387,18 +389,25 @@ def main():
     evs = [[[hip.event(), hip.event()] for _ in stage_ids] for _ in range(K)]
     # an empty event pair per step: what an event bracket adds by itself
     evp = [[hip.event(), hip.event()] for _ in range(K)]
+    # an event pair around each whole step (a replay of its own)
+    evw = [[hip.event(), hip.event()] for _ in range(K)]
 
-    def step(i, timed):
+    def step(i, timed, whole=False):
         l, p = i % L, i % P
         events = None
+        cap = not args.eager
         if timed:
             events = [0] * (2 * capi.MOE_N_STAGES)
             for k, s in enumerate(stage_ids):
                 events[2 * s], events[2 * s + 1] = evs[i][k]
-            hip.record(evp[i][0], stream.cuda_stream, not args.eager)
-            hip.record(evp[i][1], stream.cuda_stream, not args.eager)
+            hip.record(evp[i][0], stream.cuda_stream, cap)
+            hip.record(evp[i][1], stream.cuda_stream, cap)
+        if whole:
+            hip.record(evw[i][0], stream.cuda_stream, cap)
         capi.moe_layer_forward_ex(desc, weights[l], xs[p], T, out, None, None, ws, nb,
                                   stream=stream.cuda_stream, events=events)
+        if whole:
+            hip.record(evw[i][1], stream.cuda_stream, cap)
 
     # The headline loop carries no event nodes; per-kernel durations come from a
     # second pass over the same K steps with events around the stages.
@@ -414,6 +423,9 @@ def main():
         for i in range(K):
             step(i, True)
         torch.cuda.synchronize()
+        for i in range(K):
+            step(i, False, whole=True)
+        torch.cuda.synchronize()
     else:
         sh = stream.cuda_stream
         step(0, False)                       # first launches outside any capture
@@ -421,6 +433,7 @@ def main():
         gw = hip.capture(sh, lambda: [step(i, False) for i in range(W)])
         gt = hip.capture(sh, lambda: [step(i, False) for i in range(K)])
         ge = hip.capture(sh, lambda: [step(i, True) for i in range(K)])
+        gb = hip.capture(sh, lambda: [step(i, False, whole=True) for i in range(K)])
         hip.launch(gw, sh)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -429,6 +442,8 @@ def main():
         t1 = time.perf_counter()
         hip.launch(ge, sh)
         torch.cuda.synchronize()
+        hip.launch(gb, sh)
+        torch.cuda.synchronize()
 
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / K
@@ -436,12 +451,17 @@ def main():
     stage_ms = {}
     for k, s_id in enumerate(stage_ids):
         stage_ms[s_id] = [hip.elapsed_ms(evs[i][k][0], evs[i][k][1]) for i in range(K)]
-    # the event bracket holds the kernel plus the event nodes' own latency,
-    # which an empty event pair in the same replay measures; medians over the
-    # steps, as a few pairs now and then take several times their usual time
+    # The event bracket holds the kernel plus what the two event nodes add
+    # around running work.  That is measured on whole steps: a bracket around
+    # each step of a replay of its own, less the event-free time per step.
+    # (An empty event pair, also printed, takes longer than the nodes add
+    # around a kernel.)  Medians over the steps, as a few brackets now and
+    # then take several times their usual time.
     bracket_ms = float(np.median(stage_ms[capi.MOE_STAGE_GATE_UP]))
     pair_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evp]))
-    gu_ms = bracket_ms - pair_ms if bracket_ms > 2 * pair_ms else bracket_ms
+    whole_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evw]))
+    over_ms = whole_ms - ms_step
+    gu_ms = bracket_ms - over_ms if 0.0 < over_ms < 0.5 * bracket_ms else bracket_ms
     gu_bytes = float(np.mean([gate_up_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     lay_bytes = float(np.mean([layer_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
@@ -462,6 +482,7 @@ def main():
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "bracket_us": round(bracket_ms * 1e3, 3),
             "event_pair_us": round(pair_ms * 1e3, 3),
+            "bracket_overhead_us": round(over_ms * 1e3, 3),
         }
     else:
         roofline = {
@@ -473,11 +494,13 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(wl),
+            # counters were taken on the default workload (one token, all 8 experts)
+            "traffic": measured_traffic(wl) if (T == 1 and not cfg.top_p) else None,
             "bytes_per_launch": int(gu_bytes),
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "bracket_us": round(bracket_ms * 1e3, 3),
             "event_pair_us": round(pair_ms * 1e3, 3),
+            "bracket_overhead_us": round(over_ms * 1e3, 3),
         }
     names = {capi.MOE_STAGE_ROUTE: "route", capi.MOE_STAGE_BUCKET: "bucket",
              capi.MOE_STAGE_GATE_UP: "gate_up", capi.MOE_STAGE_DOWN: "down",
