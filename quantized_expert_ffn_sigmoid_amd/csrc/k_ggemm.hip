@@ -91,71 +91,31 @@ struct GgTile {
 };
 
 __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
-  if (a.nt_r % 8 == 0 && a.nt_s % 8 == 0) {
-    // Blocks are dealt to the 8 XCDs round robin; XCD x takes the n-tiles
-    // nt = x (mod 8) of every m-tile, so each XCD holds the same share of
-    // every expert's work whatever the bucket sizes (contiguous ranges of
-    // tiles would give one XCD the large experts' full tiles).  Order inside
-    // an XCD: expert, n-tile, m-tile, so the m-tiles that use the same
-    // weight rows run together and share them through that XCD's L2.
-    const int x = blockIdx.x % 8;
-    const int64_t j = blockIdx.x / 8;
-    const int R = a.nt_r / 8;
-    const int64_t routed = (int64_t)a.max_tiles * R;
-    if (j < routed) {
-      const int q0 = (int)(j / R);   // an m-tile of the expert whose run holds j
-      if (q0 >= *a.n_tiles) return false;
-      const int first = a.tile_first[q0], cnt = a.tile_cnt[q0];
-      const int64_t rem = j - (int64_t)first * R;
-      const int k = (int)(rem / cnt);
-      const int mt = first + (int)(rem - (int64_t)k * cnt);
-      t.nt = x + 8 * k;
-      t.shared = false;
-      t.e = a.tile_e[mt];
-      t.p0 = a.tile_p0[mt];
-      t.n = a.tile_n[mt];
-    } else {
-      if (a.s_tiles == 0) return false;
-      const int64_t j2 = j - routed;
-      const int k = (int)(j2 / a.s_tiles);
-      if (k >= a.nt_s / 8) return false;
-      const int mt = (int)(j2 - (int64_t)k * a.s_tiles);
-      t.nt = x + 8 * k;
-      t.shared = true;
-      t.e = 0;
-      t.p0 = mt * GG_BM;
-      t.n = min(GG_BM, a.T - t.p0);
-    }
-    return t.n > 0;
-  }
-  const int64_t total = (int64_t)a.max_tiles * a.nt_r + (int64_t)a.s_tiles * a.nt_s;
-  const int64_t per = (total + 7) / 8;
-  // Consecutive logical tiles run on one XCD (blocks are dealt to the 8 XCDs
-  // round robin) at about the same time.  Logical order: expert, n-tile,
-  // m-tile -- the m-tiles of one expert that use the same weight rows run
-  // together and share them through L2, while the activation tiles they
-  // re-read for every n-tile are small enough to stay in the last-level
-  // cache.
-  const int64_t L = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (L >= total) return false;
-  const int64_t routed = (int64_t)a.max_tiles * a.nt_r;
-  if (L < routed) {
-    // the expert's m-tiles [first, first + cnt) occupy logical tiles
-    // [first * nt_r, (first + cnt) * nt_r), so L / nt_r is one of them
-    const int q0 = (int)(L / a.nt_r);
-    if (q0 >= *a.n_tiles) return false;
-    const int first = a.tile_first[q0], cnt = a.tile_cnt[q0];
-    const int64_t rem = L - (int64_t)first * a.nt_r;
-    t.nt = (int)(rem / cnt);
-    const int mt = first + (int)(rem - (int64_t)t.nt * cnt);
+  // Blocks are dealt to the 8 XCDs round robin (block b runs on XCD b % 8).
+  // m-tiles go round robin to the XCDs, so each holds about an eighth of
+  // every large expert's tiles and of the small experts, whatever the bucket
+  // sizes; an XCD runs all n-tiles of an m-tile back to back, and they share
+  // the m-tile's activation rows through its L2.  The weight rows of an
+  // expert whose m-tiles sit on several XCDs are read once per XCD.
+  const int x = blockIdx.x % 8;
+  const int64_t j = blockIdx.x / 8;
+  const int64_t rq = (a.max_tiles + 7) / 8;
+  if (j < rq * a.nt_r) {
+    const int64_t q = j / a.nt_r;
+    t.nt = (int)(j - q * a.nt_r);
+    const int mt = x + 8 * (int)q;
+    if (mt >= *a.n_tiles) return false;
     t.shared = false;
     t.e = a.tile_e[mt];
     t.p0 = a.tile_p0[mt];
     t.n = a.tile_n[mt];
   } else {
-    const int64_t L2 = L - routed;
-    t.nt = (int)(L2 / a.s_tiles);
-    const int mt = (int)(L2 - (int64_t)t.nt * a.s_tiles);
+    if (a.s_tiles == 0 || a.nt_s == 0) return false;
+    const int64_t j2 = j - rq * a.nt_r;
+    const int64_t q = j2 / a.nt_s;
+    t.nt = (int)(j2 - q * a.nt_s);
+    const int mt = x + 8 * (int)q;
+    if (mt >= a.s_tiles) return false;
     t.shared = true;
     t.e = 0;
     t.p0 = mt * GG_BM;
@@ -562,7 +522,8 @@ hipError_t launch_ggemm(GgArgs a, bool down, int dtype, int shared_dtype, hipStr
     q.s_tiles = q.has_shared ? (q.T + GG_BM - 1) / GG_BM : 0;
     const int64_t total = (int64_t)q.max_tiles * q.nt_r + (int64_t)q.s_tiles * q.nt_s;
     if (total <= 0) return hipSuccess;
-    const unsigned blocks = (unsigned)(((total + 7) / 8) * 8);
+    const unsigned blocks = (unsigned)(8 * (((int64_t)q.max_tiles + 7) / 8 * q.nt_r +
+                                            ((int64_t)q.s_tiles + 7) / 8 * q.nt_s));
     if (wdt == MOE_I4) {
       if (down) hipLaunchKernelGGL(k_ggemm_i4<true>, dim3(blocks), dim3(GG_THREADS), 0, s, q);
       else hipLaunchKernelGGL(k_ggemm_i4<false>, dim3(blocks), dim3(GG_THREADS), 0, s, q);

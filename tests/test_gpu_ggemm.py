@@ -4,8 +4,7 @@ Batches above the decode size with bf16 activations run the expert FFNs as a
 grouped GEMM over 64-row bucket tiles.  These cases compare every output of
 the layer with the oracle on small layers whose buckets span several tiles,
 ragged last tiles and tiles of one row, for int4 and bf16 routed experts and
-int4, bf16 or no shared expert, with n-tile counts that are and are not
-multiples of 8 (the two tile maps).  The GLM-scale prefill case lives in
+int4, bf16 or no shared expert, with n-tile counts from 1 to 8.  The GLM-scale prefill case lives in
 test_gpu_layer.py (sampled tokens).
 """
 import numpy as np
@@ -43,8 +42,7 @@ def _cfg(kind):
         # K steps of 128: 6 (gate/up) and 3 (down), an odd count
         return gen.shrink(base, **dict(small, hidden=768, inter=384, seed=34))
     if kind == "i4_xcd":
-        # 8 gate/up and 8 down n-tiles: the tile map that gives each XCD the
-        # n-tiles nt = x (mod 8) of every m-tile
+        # 8 gate/up and 8 down n-tiles, more m-tiles than XCDs
         return gen.shrink(base, **dict(small, hidden=2048, inter=1024, seed=36))
     if kind == "i4_xcd_i4shared":
         return gen.shrink(base, **dict(small, hidden=2048, inter=1024, shared_dtype=gen.I4,
