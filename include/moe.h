@@ -17,7 +17,9 @@
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
  *     memory; the library allocates nothing and keeps no global state, so it
- *     is safe to call from several host threads on different streams.
+ *     is safe to call from several host threads on different streams (the
+ *     one exception, moe_layer_forward_noalloc, runs on a workspace of the
+ *     library's own, one per GPU).
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise: results are valid once the stream has
  *     reached the enqueued work.  A device-side fault surfaces at the caller's
@@ -239,6 +241,26 @@ moe_status moe_dequant_rows(int32_t dtype, const void* codes, const float* scale
 moe_status moe_requant_fp8_int4(const uint8_t* fp8, const float* block_scales, int32_t rows,
                                 int32_t cols, int32_t block, uint8_t* codes, float* scales,
                                 void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops or harnesses that forbid hipMalloc): moe_layer_forward
+ * on a workspace the library carries itself, so the caller passes only
+ * inputs and outputs.  The workspace is a device array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes per GPU (one copy on each GPU the library
+ * runs on, held until the process ends), taken on the device that `stream`
+ * runs on.  The call allocates nothing and runs the same kernels, with the
+ * same results, as moe_layer_forward.  Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (several streams or host threads)
+ * race and give undefined results; calls ordered on one stream are safe.  The
+ * array keeps the last call's contents; no kernel relies on its initial
+ * contents.  Errors: those of moe_layer_forward, and MOE_EWORKSPACE (nothing
+ * launched) when moe_workspace_bytes(d, n_tokens) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (GLM-scale layers, H 6144 and I 2048: up to 40
+ * tokens). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* d, const moe_layer_weights* w,
+                                     const void* x, int32_t n_tokens, float* out,
+                                     int32_t* topk_idx_out, float* topk_w_out, void* stream);
 
 const char* moe_status_str(moe_status s);
 

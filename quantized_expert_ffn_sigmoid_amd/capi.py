@@ -16,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
+MOE_NOALLOC_SCRATCH_BYTES = 16 << 20
 MOE_F32, MOE_BF16, MOE_I4, MOE_I2 = 0, 1, 2, 3
 MOE_ROUTER_SIGMOID_NOAUX_TC, MOE_ROUTER_SOFTMAX_TOPK = 0, 1
 (MOE_STAGE_ROUTE, MOE_STAGE_BUCKET, MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE,
@@ -77,6 +78,7 @@ def lib():
             "moe_expert_ffn": ([D, S, i32, i32, vp, vp, i32, i32, vp, vp, sz, vp], i32),
             "moe_layer_forward": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp], i32),
             "moe_layer_forward_ex": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp, O], i32),
+            "moe_layer_forward_noalloc": ([D, W, vp, i32, vp, vp, vp, vp], i32),
             "moe_rmsnorm": ([vp, i32, i32, f32, vp, vp], i32),
             "moe_stack_forward": ([D, W, i32, vp, i32, vp, vp, sz, vp], i32),
             "moe_dequant_rows": ([i32, vp, vp, i32, i32, i32, vp, vp, vp], i32),
@@ -164,6 +166,14 @@ def moe_layer_forward_ex(desc, weights: MoeLayerWeights, x, n_tokens, out, topk_
                                       _ptr(ws), ws_bytes, _stream(stream),
                                       ctypes.byref(opts) if opts is not None else None),
            "moe_layer_forward_ex")
+
+
+def moe_layer_forward_noalloc(desc, weights: MoeLayerWeights, x, n_tokens, out, topk_idx_out,
+                              topk_w_out, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), ctypes.byref(weights), _ptr(x),
+                                           n_tokens, _ptr(out), _ptr(topk_idx_out),
+                                           _ptr(topk_w_out), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 def moe_rmsnorm(x, n_tokens, hidden, eps, out, stream=None):

@@ -505,6 +505,22 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
                               stream, nullptr);
 }
 
+moe_status moe_layer_forward_noalloc(const moe_layer_desc* d, const moe_layer_weights* w,
+                                     const void* x, int32_t n_tokens, float* out,
+                                     int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  moe_status st = check_layer_args(d, w);
+  if (st != MOE_OK) return st;
+  if (n_tokens < 0) return MOE_EINVAL;
+  if (n_tokens == 0) return MOE_OK;
+  const size_t need = moe_workspace_bytes(d, n_tokens);
+  if (need > kNoAllocScratchBytes) return MOE_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (noalloc_scratch(s, &ws) != hipSuccess || !ws) return MOE_EHIP;
+  return moe_layer_forward_ex(d, w, x, n_tokens, out, topk_idx_out, topk_w_out, ws, need, stream,
+                              nullptr);
+}
+
 moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* out,
                        void* stream) {
   if (n_tokens < 0 || hidden <= 0 || !(eps >= 0.0f)) return MOE_EINVAL;

@@ -13,6 +13,8 @@ constexpr int kWave = 64;
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 32;
 constexpr int kDecodeTokens = 16;   // router logits GEMV path handles up to this many tokens
+// Size of the workspace moe_layer_forward_noalloc carries per GPU.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
 
 // ------------------------------------------------------------ device helpers
 
@@ -245,6 +247,9 @@ hipError_t launch_requant_fp8_int4(const uint8_t* fp8, const float* block_scales
                                    int32_t cols, int32_t block, uint8_t* codes, float* scales,
                                    hipStream_t s);
 bool requant_supported(int32_t cols, int32_t block);
+// Device address of the library's own workspace on the device that `stream`
+// runs on (kNoAllocScratchBytes bytes; looked up once per device).
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int32_t cols,
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);

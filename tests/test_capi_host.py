@@ -62,3 +62,23 @@ def test_validation_without_gpu():
         capi.moe_route(d, 0x1000, 0, 0x2000, 1, 0x3000, 0x4000, 0x5000, 16, stream=0)
     assert e.value.status == capi.MOE_EWORKSPACE
     assert "workspace" in capi.status_str(capi.MOE_EWORKSPACE)
+
+
+def test_noalloc_rejects_large_batches_before_any_launch():
+    """moe_layer_forward_noalloc checks its batch against the library's own
+    workspace on the host: a batch that needs more is refused with
+    MOE_EWORKSPACE and nothing is launched (no device is touched)."""
+    from quantized_expert_ffn_sigmoid_amd import capi
+    import gen
+    cfg = gen.get_config("c2")
+    d = capi.make_desc(cfg)
+    T = 64
+    assert capi.moe_workspace_bytes(d, T) > capi.MOE_NOALLOC_SCRATCH_BYTES
+    assert capi.moe_workspace_bytes(d, 40) <= capi.MOE_NOALLOC_SCRATCH_BYTES
+    st = dict(gate_up=0x10000, gate_up_stride=1 << 24, gate_up_scale=0x20000,
+              gate_up_scale_stride=1 << 24, down=0x30000, down_stride=1 << 24,
+              down_scale=0x40000, down_scale_stride=1 << 24)
+    w = capi.make_weights(dict(w_router=0x50000, bias=None, routed=st, shared=st))
+    with pytest.raises(capi.MoeError) as e:
+        capi.moe_layer_forward_noalloc(d, w, 0x60000, T, 0x70000, None, None, stream=0)
+    assert e.value.status == capi.MOE_EWORKSPACE
