@@ -37,6 +37,7 @@ SIGMOID_NOAUX_TC, SOFTMAX_TOPK = 0, 1
 # tensor ids of gen_core.h
 T_X, T_WROUTER, T_BIAS, T_GU_CODES, T_GU_SCALES, T_DN_CODES, T_DN_SCALES = 0, 1, 2, 3, 4, 5, 6
 T_GU_BF16, T_DN_BF16, T_ZIPF_PERM, T_GU_I8, T_DN_I8 = 7, 8, 9, 10, 11
+T_GU_BYTES, T_DN_BYTES = 12, 13
 
 SCALE_LO, SCALE_WIDTH = 0.01, 0.04   # per-row scales U(0.01, 0.05)
 
@@ -67,6 +68,9 @@ class Config:
     zipf_s: float = 1.1
     zipf_lambda: float = 0.0
     top_p: float = 0.0             # adaptive expert top-p (0: off)
+    full_codes: bool = False       # integer codes as uniform bytes: the whole range of
+                                   # each container (int4 [-8, 7], int2 [-2, 1], int8
+                                   # [-128, 127]) instead of the symmetric draws
 
 
 # Router bias of the Zipf-skewed workload, by popularity rank: calibrated once
@@ -172,9 +176,10 @@ def host_lib():
         lib.gen_fill_u64.argtypes = [vp, i64, u64, i32, i32, i32]
         lib.gen_int2_from_int4.argtypes = [vp, vp, i64, i64, vp, vp]
         lib.gen_fill_int8.argtypes = [vp, u64, i32, i32, i32, i64]
+        lib.gen_fill_bytes.argtypes = [vp, u64, i32, i32, i32, i64]
         for fn in (lib.gen_fill_int4, lib.gen_fill_scales, lib.gen_fill_normal_f32,
                    lib.gen_fill_normal_bf16, lib.gen_fill_u64, lib.gen_int2_from_int4,
-                   lib.gen_fill_int8):
+                   lib.gen_fill_int8, lib.gen_fill_bytes):
             fn.restype = None
         _host = lib
     return _host
@@ -195,6 +200,13 @@ def int8_codes(seed, layer, tensor, expert, rows, cols) -> np.ndarray:
     """int8 codes uniform on {-127..127}, row-major [rows][cols] bytes."""
     out = np.empty((rows, cols), dtype=np.uint8)
     host_lib().gen_fill_int8(_p(out), seed, layer, tensor, expert, out.size)
+    return out
+
+
+def code_bytes(seed, layer, tensor, expert, rows, row_bytes) -> np.ndarray:
+    """Uniform bytes [rows][row_bytes]: packed codes over a container's whole range."""
+    out = np.empty((rows, row_bytes), dtype=np.uint8)
+    host_lib().gen_fill_bytes(_p(out), seed, layer, tensor, expert, out.size)
     return out
 
 
@@ -334,6 +346,14 @@ def expert(cfg: Config, layer: int, e: int, dtype: Optional[int] = None, shared:
     if dtype is None:
         dtype = cfg.shared_dtype if shared else cfg.expert_dtype
     eid = cfg.n_experts if shared else e
+    if cfg.full_codes and dtype in (I4, I2, I8):
+        ppb = {I4: 2, I2: 4, I8: 1}[dtype]
+        mult = 1.0 / 16.0 if dtype == I8 else 1.0
+        gu = code_bytes(cfg.seed, layer, T_GU_BYTES, eid, 2 * I, H // ppb)
+        dn = code_bytes(cfg.seed, layer, T_DN_BYTES, eid, H, I // ppb)
+        gus = scales(cfg.seed, layer, T_GU_SCALES, eid, 2 * I, scale_mult(cfg, H) * mult)
+        dns = scales(cfg.seed, layer, T_DN_SCALES, eid, H, scale_mult(cfg, I) * mult)
+        return dict(dtype=dtype, gate_up=gu, gate_up_scale=gus, down=dn, down_scale=dns)
     if dtype == I8:
         gu = int8_codes(cfg.seed, layer, T_GU_I8, eid, 2 * I, H)
         gus = scales(cfg.seed, layer, T_GU_SCALES, eid, 2 * I, scale_mult(cfg, H) / 16.0)

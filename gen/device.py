@@ -173,6 +173,8 @@ def generate_device_layer(cfg: Config, layer: int, device, dtype: Optional[int] 
     (int4 layer, int2 layer) sharing router and shared expert."""
     import torch
     dtype = cfg.expert_dtype if dtype is None else dtype
+    if cfg.full_codes:
+        raise ValueError("full-range codes are generated on the host: use upload_host_layer")
     stream = torch.cuda.current_stream(device).cuda_stream
     w, b = router(cfg, layer)
     w_t = _upload(w, device)

@@ -39,7 +39,9 @@ enum {
   GEN_T_DN_BF16 = 8,    /* down bf16 weights [H][I]                     */
   GEN_T_ZIPF_PERM = 9,  /* expert popularity permutation                */
   GEN_T_GU_I8 = 10,     /* gate/up int8 codes [2I][H]                   */
-  GEN_T_DN_I8 = 11      /* down int8 codes [H][I]                       */
+  GEN_T_DN_I8 = 11,     /* down int8 codes [H][I]                       */
+  GEN_T_GU_BYTES = 12,  /* gate/up codes as uniform bytes (full range)  */
+  GEN_T_DN_BYTES = 13   /* down codes as uniform bytes (full range)     */
 };
 
 GEN_FN uint64_t gen_mix64(uint64_t z) {
@@ -87,6 +89,13 @@ GEN_FN uint16_t gen_int8_pair(uint64_t key, uint64_t pair_index) {
   int lo = (int)gen_below((uint32_t)(r & 0xFFFFFFFFu), 255u) - 127;
   int hi = (int)gen_below((uint32_t)(r >> 32), 255u) - 127;
   return (uint16_t)(((unsigned)lo & 0xFFu) | (((unsigned)hi & 0xFFu) << 8));
+}
+
+/* A uniform byte: byte i % 8 of draw i / 8.  As packed codes it covers the
+ * whole two's-complement range of every container: int4 [-8, 7], int2
+ * [-2, 1], int8 [-128, 127]. */
+GEN_FN uint8_t gen_byte(uint64_t key, uint64_t i) {
+  return (uint8_t)(gen_draw(key, i >> 3) >> (8 * (i & 7)));
 }
 
 /* Signed value of nibble j (0 or 1) of a packed int4 byte. */

@@ -196,6 +196,11 @@ enum {
 };
 typedef struct {
   void* const* events;     /* (host) [2*MOE_N_STAGES] hipEvent_t, nullable */
+  float* h_f32;            /* test hook, nullable: receives the SwiGLU output h  */
+                           /* of every routed row before any bf16 rounding,      */
+                           /* fp32 [n_tokens*top_k][I] by bucket position (rows  */
+                           /* past the grouped slots untouched), then the shared */
+                           /* expert's [n_tokens][n_shared*I]                    */
 } moe_launch_opts;
 
 moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_layer_weights* w,

@@ -95,6 +95,7 @@ def lib():
             "orc_route": [D, vp, vp, vp, i32, vp, vp, vp],
             "orc_bucket": [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp],
             "orc_expert_ffn": [D, S, i32, i32, vp, vp, i32, i32, vp],
+            "orc_expert_h": [D, S, i32, i32, vp, vp, i32, i32, vp, vp],
             "orc_layer_forward": [D, vp, vp, S, S, vp, i32, vp, vp, vp],
             "orc_layer_forward_per_token": [D, vp, vp, S, S, vp, i32, vp],
             "orc_layer_band": [D, vp, vp, S, S, vp, i32, dbl, vp],
@@ -225,6 +226,23 @@ def expert_ffn(d: Desc, eset: ExpertSet, e: int, x, rows=None, n_rows=None, row_
     return y
 
 
+def expert_h(d: Desc, eset: ExpertSet, e: int, x, rows=None, n_rows=None, row_div=1,
+             inter=None, with_scale=False):
+    """The expert's SwiGLU output h [n_rows][inter] in fp64, before any
+    rounding; with_scale: (h, e) with e the first-order scale of the error that
+    rounding the terms of g and u makes in h (a test tolerance)."""
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        n_rows = rows.shape[0]
+    inter = inter or d.inter
+    h = np.empty((n_rows, inter), dtype=np.float64)
+    es = np.empty((n_rows, inter), dtype=np.float64) if with_scale else None
+    if n_rows:
+        _check(lib().orc_expert_h(ctypes.byref(d.c()), ctypes.byref(eset.c), e, inter, _p(x),
+                                  _p(rows), n_rows, row_div, _p(h), _p(es)))
+    return (h, es) if with_scale else h
+
+
 def layer_forward(d: Desc, w_router, bias, routed: ExpertSet, shared: Optional[ExpertSet], x,
                   n_tokens):
     out = np.empty((n_tokens, d.hidden), dtype=np.float64)
@@ -250,15 +268,16 @@ def layer_forward_per_token(d: Desc, w_router, bias, routed: ExpertSet,
 
 
 def layer_band(d: Desc, w_router, bias, routed: ExpertSet, shared: Optional[ExpertSet], x,
-               n_tokens, rel_window: float) -> np.ndarray:
-    """Output band of the bf16 rounding of h (see moe_oracle.h); zeros for f32
-    activations."""
+               n_tokens, window: float) -> np.ndarray:
+    """Output band of the bf16 rounding of h (see moe_oracle.h): an h is
+    ambiguous within window * (its error scale) of a rounding midpoint; zeros
+    for f32 activations."""
     band = np.empty((n_tokens, d.hidden), dtype=np.float64)
     if n_tokens:
         _check(lib().orc_layer_band(ctypes.byref(d.c()), _p(w_router), _p(bias),
                                     ctypes.byref(routed.c),
                                     ctypes.byref(shared.c) if shared else None, _p(x),
-                                    n_tokens, float(rel_window), _p(band)))
+                                    n_tokens, float(window), _p(band)))
     return band
 
 
@@ -303,14 +322,14 @@ def layer_forward_host(hl, x: np.ndarray, desc: Optional[Desc] = None):
     return layer_forward(d, hl.w_router, hl.bias, routed, shared_set_from_host_layer(hl), x, T)
 
 
-def layer_band_host(hl, x: np.ndarray, rel_window: float, desc: Optional[Desc] = None):
+def layer_band_host(hl, x: np.ndarray, window: float, desc: Optional[Desc] = None):
     """layer_band for a gen.HostLayer, generating only the selected experts."""
     d = desc or Desc.from_config(hl.cfg, expert_dtype=hl.dtype)
     T = x.shape[0]
     idx, _, _ = route(d, hl.w_router, hl.bias, x, T)
     routed = expert_set_from_host_layer(hl, np.unique(idx))
     return layer_band(d, hl.w_router, hl.bias, routed, shared_set_from_host_layer(hl), x, T,
-                      rel_window)
+                      window)
 
 
 def stack_forward_host(layers, x: np.ndarray, eps: float):

@@ -383,23 +383,43 @@ int orc_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t
 
 /* ----------------------------------------------------------- expert FFN -- */
 
-/* SwiGLU expert on one activation vector xv[H] -> y[H] ("iliria" README, "What's
- * implemented": routed-expert SwiGLU).  g_r and u_r are the gate and up rows
- * applied to x; h_r = silu(g_r) * u_r with silu(v) = v / (1 + exp(-v)); when
- * activations are bf16, h is rounded to float and then to bf16 (round to
- * nearest even) before the down projection; y_o = sum_r down[o][r] * h_r. */
-static void ffn_one(int32_t dtype, int act_bf16, const void* gu, const float* gus, const void* dn,
-                    const float* dns, int64_t H, int64_t I, const double* xv, double* hbuf,
-                    double* y) {
+/* First half of a SwiGLU expert ("iliria" README, "What's implemented":
+ * routed-expert SwiGLU, gate and up over one activation): g_r and u_r are the
+ * gate and up rows applied to xv[H]; h_r = silu(g_r) * u_r with silu(v) =
+ * v / (1 + exp(-v)), in fp64, not rounded.
+ * With ebuf (a test tolerance, not part of the layer), also the scale of the
+ * error that rounding the terms of g and u makes in h, to first order:
+ * e_r = |silu'(g) u| * sum_c |w_gc x_c| + |silu(g)| * sum_c |w_uc x_c|, with
+ * silu'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)). */
+static void swiglu_rows(int32_t dtype, const void* gu, const float* gus, int64_t H, int64_t I,
+                        const double* xv, double* hbuf, double* ebuf) {
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < I; ++r) {
     double g = 0.0, u = 0.0;
     for (int64_t c = 0; c < H; ++c) g += weight_at(dtype, gu, gus, H, r, c) * xv[c];
     for (int64_t c = 0; c < H; ++c) u += weight_at(dtype, gu, gus, H, I + r, c) * xv[c];
     double h = g / (1.0 + exp(-g)) * u;
-    if (act_bf16) h = bf16_to_double(float_to_bf16((float)h));
     hbuf[r] = h;
+    if (ebuf) {
+      double ag = 0.0, au = 0.0;
+      for (int64_t c = 0; c < H; ++c) ag += fabs(weight_at(dtype, gu, gus, H, r, c) * xv[c]);
+      for (int64_t c = 0; c < H; ++c) au += fabs(weight_at(dtype, gu, gus, H, I + r, c) * xv[c]);
+      const double sg = 1.0 / (1.0 + exp(-g));
+      const double dsilu = sg * (1.0 + g * (1.0 - sg));
+      ebuf[r] = fabs(dsilu * u) * ag + fabs(g * sg) * au;
+    }
   }
+}
+
+/* SwiGLU expert on one activation vector xv[H] -> y[H]: h from swiglu_rows;
+ * when activations are bf16, h is rounded to float and then to bf16 (round to
+ * nearest even) before the down projection; y_o = sum_r down[o][r] * h_r. */
+static void ffn_one(int32_t dtype, int act_bf16, const void* gu, const float* gus, const void* dn,
+                    const float* dns, int64_t H, int64_t I, const double* xv, double* hbuf,
+                    double* y) {
+  swiglu_rows(dtype, gu, gus, H, I, xv, hbuf, NULL);
+  if (act_bf16)
+    for (int64_t r = 0; r < I; ++r) hbuf[r] = bf16_to_double(float_to_bf16((float)hbuf[r]));
 #pragma omp parallel for schedule(static)
   for (int64_t o = 0; o < H; ++o) {
     double acc = 0.0;
@@ -424,6 +444,28 @@ static int ffn_token(const orc_desc* d, const orc_expert_set* set, int32_t e, in
   for (int64_t c = 0; c < H; ++c) xv[c] = x_at(x, d->act_bf16, t * H + c);
   ffn_one(set->dtype, d->act_bf16, set->gate_up[e], set->gate_up_scale ? set->gate_up_scale[e] : 0,
           set->down[e], set->down_scale ? set->down_scale[e] : 0, H, I, xv, hbuf, y);
+  return ORC_OK;
+}
+
+/* The SwiGLU output h (fp64, before any rounding) of one expert over a list
+ * of rows, as orc_expert_ffn evaluates it: h[i][r] for token rows[i] / row_div
+ * (rows NULL: token i); inter is the expert's intermediate size.  e
+ * (nullable) receives the error scale of each h (swiglu_rows). */
+int orc_expert_h(const orc_desc* d, const orc_expert_set* set, int32_t expert, int32_t inter,
+                 const void* x, const int32_t* rows, int32_t n_rows, int32_t row_div,
+                 double* h, double* e) {
+  if (!d || d->hidden <= 0 || inter <= 0 || row_div <= 0) return ORC_EINVAL;
+  if (!set_has(set, expert)) return ORC_EMISSING;
+  const int64_t H = d->hidden;
+  double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+  for (int32_t i = 0; i < n_rows; ++i) {
+    const int64_t t = rows ? rows[i] / row_div : i;
+    for (int64_t c = 0; c < H; ++c) xv[c] = x_at(x, d->act_bf16, t * H + c);
+    swiglu_rows(set->dtype, set->gate_up[expert],
+                set->gate_up_scale ? set->gate_up_scale[expert] : 0, H, inter, xv,
+                h + (int64_t)i * inter, e ? e + (int64_t)i * inter : NULL);
+  }
+  free(xv);
   return ORC_OK;
 }
 
@@ -452,22 +494,22 @@ int orc_expert_ffn(const orc_desc* d, const orc_expert_set* set, int32_t expert,
  * kernel that accumulates in fp32 in another order lands a value lying very
  * near a rounding midpoint on either side of it, and both roundings are
  * correct results of the layer as defined ("muse-glimmer-intel-serve"
- * introduction: the low-precision twin defines the deviation band).  For
- * every h whose float value lies within rel_window * |h| of the midpoint
- * between its two bf16 neighbours, the other neighbour is also valid; the
- * band of an output is the largest change such alternatives can make to it:
+ * introduction: the low-precision twin defines the deviation band).  An h is
+ * ambiguous when its float value lies within window * e of the midpoint
+ * between its two bf16 neighbours, e being the scale of the error that
+ * rounding the terms of its sums makes in h (swiglu_rows); window is then a
+ * multiple of the unit roundoff that covers a kernel's accumulation error.
+ * For every ambiguous h the other neighbour is also valid; the band of an
+ * output is the largest change such alternatives can make to it:
  *   band[t][o] = sum_j |w_tj| * sum_{r ambiguous} |down_o,r| * |h_alt - h_bf16|
  * plus the same sum over the shared expert (weight 1).  Zero when
  * activations are f32. */
 static void ffn_band_one(int32_t dtype, const void* gu, const float* gus, const void* dn,
                          const float* dns, int64_t H, int64_t I, const double* xv,
-                         double rel_window, double weight, double* dh, double* band) {
-#pragma omp parallel for schedule(static)
+                         double window, double weight, double* dh, double* eb, double* band) {
+  swiglu_rows(dtype, gu, gus, H, I, xv, dh, eb);
   for (int64_t r = 0; r < I; ++r) {
-    double g = 0.0, u = 0.0;
-    for (int64_t c = 0; c < H; ++c) g += weight_at(dtype, gu, gus, H, r, c) * xv[c];
-    for (int64_t c = 0; c < H; ++c) u += weight_at(dtype, gu, gus, H, I + r, c) * xv[c];
-    const float hf = (float)(g / (1.0 + exp(-g)) * u);
+    const float hf = (float)dh[r];
     uint32_t bits;
     memcpy(&bits, &hf, 4);
     dh[r] = 0.0;
@@ -477,7 +519,7 @@ static void ffn_band_one(int32_t dtype, const void* gu, const float* gus, const 
     memcpy(&lo, &lo_bits, 4);
     memcpy(&hi, &hi_bits, 4);
     const double mid = 0.5 * ((double)lo + (double)hi);
-    if (fabs((double)hf - mid) <= rel_window * fabs((double)hf)) dh[r] = fabs((double)hi - (double)lo);
+    if (fabs((double)hf - mid) <= window * eb[r]) dh[r] = fabs((double)hi - (double)lo);
   }
 #pragma omp parallel for schedule(static)
   for (int64_t o = 0; o < H; ++o) {
@@ -490,8 +532,8 @@ static void ffn_band_one(int32_t dtype, const void* gu, const float* gus, const 
 
 int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
                    const orc_expert_set* routed, const orc_expert_set* shared, const void* x,
-                   int32_t n_tokens, double rel_window, double* band) {
-  if (!desc_ok(d) || rel_window < 0.0) return ORC_EINVAL;
+                   int32_t n_tokens, double window, double* band) {
+  if (!desc_ok(d) || !(window >= 0.0)) return ORC_EINVAL;
   const int64_t H = d->hidden, K = d->top_k;
   for (int64_t i = 0; i < (int64_t)n_tokens * H; ++i) band[i] = 0.0;
   if (n_tokens == 0 || !d->act_bf16) return ORC_OK;
@@ -500,6 +542,7 @@ int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
   double* w64 = (double*)malloc(sizeof(double) * (size_t)n_tokens * (size_t)K);
   double* xv = (double*)malloc(sizeof(double) * (size_t)H);
   double* dh = (double*)malloc(sizeof(double) * (size_t)Is);
+  double* eb = (double*)malloc(sizeof(double) * (size_t)Is);
   int rc = orc_route(d, w_router, bias, x, n_tokens, idx, NULL, w64);
   for (int64_t t = 0; t < n_tokens && rc == ORC_OK; ++t) {
     for (int64_t c = 0; c < H; ++c) xv[c] = x_at(x, 1, t * H + c);
@@ -512,8 +555,8 @@ int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
       }
       ffn_band_one(routed->dtype, routed->gate_up[e],
                    routed->gate_up_scale ? routed->gate_up_scale[e] : 0, routed->down[e],
-                   routed->down_scale ? routed->down_scale[e] : 0, H, d->inter, xv, rel_window,
-                   fabs(w64[t * K + j]), dh, band + t * H);
+                   routed->down_scale ? routed->down_scale[e] : 0, H, d->inter, xv, window,
+                   fabs(w64[t * K + j]), dh, eb, band + t * H);
     }
     if (rc == ORC_OK && d->n_shared > 0) {
       if (!set_has(shared, 0)) {
@@ -522,14 +565,15 @@ int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
       }
       ffn_band_one(shared->dtype, shared->gate_up[0],
                    shared->gate_up_scale ? shared->gate_up_scale[0] : 0, shared->down[0],
-                   shared->down_scale ? shared->down_scale[0] : 0, H, Is, xv, rel_window, 1.0,
-                   dh, band + t * H);
+                   shared->down_scale ? shared->down_scale[0] : 0, H, Is, xv, window, 1.0,
+                   dh, eb, band + t * H);
     }
   }
   free(idx);
   free(w64);
   free(xv);
   free(dh);
+  free(eb);
   return rc;
 }
 

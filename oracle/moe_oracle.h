@@ -58,6 +58,12 @@ int orc_bucket(int32_t n_tokens, int32_t top_k, int32_t n_experts, const int32_t
 int orc_expert_ffn(const orc_desc* d, const orc_expert_set* set, int32_t expert, int32_t inter,
                    const void* x, const int32_t* rows, int32_t n_rows, int32_t row_div,
                    double* y);
+/* The expert's SwiGLU output h[n_rows][inter] in fp64 before any rounding
+ * (rows as orc_expert_ffn); e (nullable) receives each h's error scale
+ * |silu'(g) u| sum|w_g x| + |silu(g)| sum|w_u x| (a test tolerance). */
+int orc_expert_h(const orc_desc* d, const orc_expert_set* set, int32_t expert, int32_t inter,
+                 const void* x, const int32_t* rows, int32_t n_rows, int32_t row_div,
+                 double* h, double* e);
 int orc_layer_forward(const orc_desc* d, const float* w_router, const float* bias,
                       const orc_expert_set* routed, const orc_expert_set* shared, const void* x,
                       int32_t n_tokens, double* out, int32_t* topk_idx, float* topk_w);
@@ -66,11 +72,13 @@ int orc_layer_forward_per_token(const orc_desc* d, const float* w_router, const 
                                 const void* x, int32_t n_tokens, double* out);
 /* Output band of the bf16 rounding of h (act bf16 only; zero otherwise):
  * band[t][o] bounds the change of out[t][o] when every h whose float value
- * lies within rel_window * |h| of a bf16 rounding midpoint takes the other
- * rounding.  A test tolerance, not part of the layer. */
+ * lies within window * e of a bf16 rounding midpoint takes the other
+ * rounding, e being the first-order scale of the error that rounding the
+ * terms of g and u makes in h (orc_expert_h).  A test tolerance, not part of
+ * the layer. */
 int orc_layer_band(const orc_desc* d, const float* w_router, const float* bias,
                    const orc_expert_set* routed, const orc_expert_set* shared, const void* x,
-                   int32_t n_tokens, double rel_window, double* band);
+                   int32_t n_tokens, double window, double* band);
 int orc_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, double eps, float* out);
 int orc_residual_add(float* x, const double* y, int64_t n);
 void orc_set_threads(int32_t n);

@@ -52,7 +52,7 @@ class MoeLayerWeights(ctypes.Structure):
 
 
 class MoeLaunchOpts(ctypes.Structure):
-    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p))]
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("h_f32", ctypes.c_void_p)]
 
 
 _lib = None
@@ -154,13 +154,17 @@ def moe_layer_forward(desc, weights: MoeLayerWeights, x, n_tokens, out, topk_idx
 
 
 def moe_layer_forward_ex(desc, weights: MoeLayerWeights, x, n_tokens, out, topk_idx_out,
-                         topk_w_out, ws, ws_bytes, stream=None, events=None):
-    """events: optional list of 2*MOE_N_STAGES raw hipEvent_t handles (ints)."""
+                         topk_w_out, ws, ws_bytes, stream=None, events=None, h_f32=None):
+    """events: optional list of 2*MOE_N_STAGES raw hipEvent_t handles (ints);
+    h_f32: optional device buffer for the fp32 h before rounding (test hook)."""
     opts = None
     keep = None
-    if events is not None:
-        keep = (ctypes.c_void_p * len(events))(*[e or None for e in events])
-        opts = MoeLaunchOpts(ctypes.cast(keep, ctypes.POINTER(ctypes.c_void_p)))
+    if events is not None or h_f32 is not None:
+        evp = None
+        if events is not None:
+            keep = (ctypes.c_void_p * len(events))(*[e or None for e in events])
+            evp = ctypes.cast(keep, ctypes.POINTER(ctypes.c_void_p))
+        opts = MoeLaunchOpts(evp, _ptr(h_f32))
     _check(lib().moe_layer_forward_ex(ctypes.byref(desc), ctypes.byref(weights), _ptr(x),
                                       n_tokens, _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
                                       _ptr(ws), ws_bytes, _stream(stream),

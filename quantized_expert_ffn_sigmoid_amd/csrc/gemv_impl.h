@@ -27,6 +27,7 @@
 
 #include "moe_internal.h"
 #include "route_device.h"
+#include "unpack.h"
 
 namespace moe {
 
@@ -100,10 +101,9 @@ __device__ __forceinline__ void i8_half_fma(const uint32_t (&gr)[4], const float
                                             int e0, float (&acc)[NT]) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const uint32_t w = gr[d] ^ 0x80808080u;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float q = fmaf((float)((w >> (8 * b)) & 0xFFu), 1.0f / 512.0f, -120.0f / 512.0f);
+      const float q = i8_unpack_f32(gr[d], b);
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = fmaf(q, x[n][e0 + 4 * d + b], acc[n]);
     }
@@ -121,15 +121,9 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
   if constexpr (WDT == MOE_I4) {
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      // offset-binary nibbles, even ones in lo's bytes, odd ones in hi's
-      const uint32_t lo = (gr[d] ^ 0x08080808u) & 0x0F0F0F0Fu;
-      const uint32_t hi = ((gr[d] >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;
-      const f32x2 l01 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-      const f32x2 l23 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-      const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-      const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-      const float ql[4] = {l01.x, l01.y, l23.x, l23.y};
-      const float qh[4] = {h01.x, h01.y, h23.x, h23.y};
+      // offset-binary codes: even ones in ql, odd ones in qh
+      float ql[4], qh[4];
+      i4_unpack_f32(gr[d], ql, qh);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -147,13 +141,10 @@ __device__ __forceinline__ void granule_fma(const uint32_t (&gr)[Fmt<WDT>::DW],
   } else if constexpr (WDT == MOE_I2) {
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      const uint32_t w = gr[d] ^ 0xAAAAAAAAu;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t c = (w >> (2 * jj)) & 0x03030303u;
-        const f32x2 c01 = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-        const f32x2 c23 = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-        const float q[4] = {c01.x, c01.y, c23.x, c23.y};
+        float q[4];
+        i2_unpack_f32(gr[d], jj, q);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
 #pragma unroll
@@ -285,7 +276,7 @@ struct Job {
 // h[hrow[n]][r]; otherwise y[yrow[n]][r] = scaled dot.
 template <int WDT, int KSL, int NT, int ABF16, bool PAIR>
 __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, int nt,
-                          void* dst, const int64_t* drow) {
+                          void* dst, const int64_t* drow, float* probe) {
   using F = Fmt<WDT>;
   constexpr int EPG = F::EPG, GB = F::GB, DW = F::DW, GPL = KSL / EPG;
   constexpr int NM = PAIR ? 2 : 1;
@@ -392,6 +383,7 @@ __device__ void job_chunk(const Job& jb, const void* src, const int64_t* xoff, i
                     reinterpret_cast<uint16_t*>(dst)[drow[n] * jb.rows + r] = f32_to_bf16_bits(hv);
                   else
                     reinterpret_cast<float*>(dst)[drow[n] * jb.rows + r] = hv;
+                  if (probe) probe[drow[n] * jb.rows + r] = hv;
                 } else {
                   reinterpret_cast<float*>(dst)[drow[n] * jb.rows + r] = red[0][n] * sa;
                 }
@@ -967,6 +959,7 @@ __device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
         __syncthreads();
         const int ntw = (NT2 == 2 && nt >= 2) ? nt : 1;
         const bool sl = !DOWN && a.out_sliced;
+        float* probe = DOWN ? nullptr : (bw.shared ? a.hp_s : a.hp);
         for (int t = threadIdx.x; t < ntw * nr; t += kThreads) {
           const int n = t / nr, rl = t - n * nr;
           const int64_t col = jb.r0 + rl;
@@ -975,6 +968,7 @@ __device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
             reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16_bits(L.out[n][rl]);
           else
             reinterpret_cast<float*>(out)[o] = L.out[n][rl];
+          if (probe) probe[dr[n] * jb.rows + col] = L.out[n][rl];
         }
         __syncthreads();
         continue;
@@ -982,9 +976,11 @@ __device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
     }
     if constexpr (kChunk) {
       if (NT2 == 2 && nt >= 2)
-        job_chunk<WDT, KSL, NT2, ABF16, !DOWN>(jb, in, xo, nt, out, dr);
+        job_chunk<WDT, KSL, NT2, ABF16, !DOWN>(jb, in, xo, nt, out, dr,
+                                               DOWN ? nullptr : (bw.shared ? a.hp_s : a.hp));
       else
-        job_chunk<WDT, KSL, 1, ABF16, !DOWN>(jb, in, xo, 1, out, dr);
+        job_chunk<WDT, KSL, 1, ABF16, !DOWN>(jb, in, xo, 1, out, dr,
+                                             DOWN ? nullptr : (bw.shared ? a.hp_s : a.hp));
     }
   }
 }

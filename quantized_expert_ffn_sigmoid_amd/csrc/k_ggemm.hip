@@ -22,16 +22,17 @@
 // rows padded to 272 bytes so that the 16-byte operand reads of 16 lanes fall
 // on distinct banks.  Weights go straight from HBM to registers: lane l reads
 // 16 bytes of weight row (l % 16) for its K group (l / 16), which are exactly
-// the operand elements it supplies.  int4 codes become exact bf16 values with
-// a shift and an AND-OR per pair of codes: the offset-binary code q + 8 in the
-// top mantissa bits of 1.0 is (24 + q) / 16.  The offset is removed in the
-// epilogue with the row sums of the activations (k_rowsum_bf16, one pass over
-// x and one over h).  The
-// pairing of nibbles (j, j + 4) in each converted register is matched by
-// storing each group of 8 activations in LDS in the order 0,4,1,5,2,6,3,7.
+// the operand elements it supplies.  int4 codes become the exact bf16 values
+// q + 8 (the offset-binary code), two per packed fp8 -> bf16 conversion; the
+// offset, 8 code units, is removed in the epilogue with the row sums of the
+// activations (k_rowsum_bf16, one pass over x and one over h).  The pairing
+// of the converted codes ((0, 2), (4, 6), (1, 3), (5, 7) of each dword) is
+// matched by storing each group of 8 activations in the order
+// 0,2,4,6,1,3,5,7.
 // bf16 weights need neither step.  Per-row scales commute with the K sum and
 // are applied in the epilogue, as in the decode kernels.
 #include "moe_internal.h"
+#include "unpack.h"
 
 namespace moe {
 
@@ -44,41 +45,22 @@ constexpr int GG_BK = 128;         // K per step
 constexpr int GG_WAVES = 4;
 constexpr int GG_THREADS = GG_WAVES * 64;
 constexpr int GG_NW = 64;          // weight rows per wave
-constexpr float GG_OFF = 24.0f;    // int4 operand = (GG_OFF + q) / GG_DIV
-constexpr float GG_DIV = 16.0f;
+constexpr float GG_OFF = 8.0f;     // int4 operand = GG_OFF + q
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4g v) { return __builtin_bit_cast(bf16x8, v); }
 
-// 8 int4 codes (one dword, low nibble first) -> 4 registers of bf16 pairs
-// (code j, code j + 4).  The offset-binary code u = q + 8 goes to the top four
-// mantissa bits of 1.0, giving 1 + u / 16 = (24 + q) / 16 exactly; of the
-// exact encodings with an implicit leading one this has the smallest offset
-// relative to the code, which keeps the fp32 accumulation error small.
-// The mask and the constant come in registers so that each register takes
-// one shift and one v_and_or_b32 (which cannot encode literal operands).
-__device__ __forceinline__ uint32_t and_or(uint32_t v, uint32_t m, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(v), "v"(m), "v"(c));
-  return r;
-}
-
-__device__ __forceinline__ u32x4g i4_to_bf16(uint32_t w, uint32_t mask, uint32_t one) {
-  const uint32_t u = w ^ 0x88888888u;
+// int4 codes become the bf16 values q + 8 by i4_to_bf16 (unpack.h); the
+// offset of 8 against codes of rms ~4.3 keeps the fp32 accumulation error
+// near that of the codes themselves.
+//
+// Reorder 8 bf16 activations (x0..x7 in 4 dwords) to x0,x2,x4,x6,x1,x3,x5,x7,
+// the order of the codes i4_to_bf16 yields.
+__device__ __forceinline__ u32x4g perm_0246(u32x4g d) {
   u32x4g r;
-  r.x = and_or(u << 3, mask, one);
-  r.y = and_or(u >> 1, mask, one);
-  r.z = and_or(u >> 5, mask, one);
-  r.w = and_or(u >> 9, mask, one);
-  return r;
-}
-
-// Reorder 8 bf16 activations (x0..x7 in 4 dwords) to x0,x4,x1,x5,x2,x6,x3,x7.
-__device__ __forceinline__ u32x4g perm_0415(u32x4g d) {
-  u32x4g r;
-  r.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);
-  r.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);
-  r.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);
-  r.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);
+  r.x = __builtin_amdgcn_perm(d.y, d.x, 0x05040100u);
+  r.y = __builtin_amdgcn_perm(d.w, d.z, 0x05040100u);
+  r.z = __builtin_amdgcn_perm(d.y, d.x, 0x07060302u);
+  r.w = __builtin_amdgcn_perm(d.w, d.z, 0x07060302u);
   return r;
 }
 
@@ -215,9 +197,9 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 
   // Activation loads: thread (rb = tid / 16, p = tid % 16) moves stored
   // position p of tile rows rb + 16 i (i < 4), which holds logical piece
-  // p ^ rb.  int4 weights pair nibbles (j, j + 4), so their activations are
-  // read from rows stored in the matching order (x_p, and h as gate/up writes
-  // it).
+  // p ^ rb.  int4 weights yield their codes in the order 0,2,4,6,1,3,5,7 of
+  // each group of 8, so their activations are read from rows stored in that
+  // order (x_p, and h as gate/up writes it).
   const int xp = threadIdx.x & 15, xrb = threadIdx.x >> 4;
   const int xc = xp ^ xrb;   // logical piece
   const uint8_t* xsrc[MS];
@@ -285,7 +267,6 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // The loop is unrolled by U so that every register set has a fixed name;
   // all loads are unconditional (steps past the end repeat the last one) and,
   // without GUARD, the body has no branches.
-  const uint32_t vmask = 0x00780078u, vone = 0x3F803F80u;
   for (int kt0 = 0; kt0 < nk; kt0 += U) {
 #pragma unroll
     for (int st = 0; st < U; ++st) {
@@ -320,7 +301,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
             if constexpr (I4) {
               const u32x4g wq = wbuf[wsl][ns][st % GRP];
               const uint32_t w = d == 0 ? wq.x : d == 1 ? wq.y : d == 2 ? wq.z : wq.w;
-              bv = as_bf16x8(i4_to_bf16(w, vmask, vone));
+              bv = as_bf16x8(i4_to_bf16(w));
             } else {
               bv = as_bf16x8(wbuf[wsl][ns][d]);
             }
@@ -337,8 +318,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 
   // epilogue: lane holds rows m = 16 ms + 4 kg + j of column (weight row) ln
   // of each N-subtile.  gate/up of int4 experts writes h in the order their
-  // down projection reads it (nibble pairs (j, j + 4) within groups of 8).
-  const float mul = I4 ? GG_DIV : 1.0f;
+  // down projection reads it (0,2,4,6,1,3,5,7 within groups of 8).
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms) {
 #pragma unroll
@@ -350,16 +330,19 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
       if constexpr (DOWN) {
         float* yrow = (t.shared ? a.y_s : a.y) + orow * a.H;
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) yrow[wrow[ns]] = sc[ns] * fmaf(mul, acc[ms][ns][j], -off);
+        for (int ns = 0; ns < 4; ++ns) yrow[wrow[ns]] = sc[ns] * (acc[ms][ns][j] - off);
       } else {
         uint16_t* hrow = (t.shared ? a.h_s : a.h) + orow * rows;
+        float* prow = t.shared ? a.hp_s : a.hp;
 #pragma unroll
         for (int ns = 0; ns < 2; ++ns) {
-          const float g = sc[ns] * fmaf(mul, acc[ms][ns][j], -off);
-          const float u = sc[ns + 2] * fmaf(mul, acc[ms][ns + 2][j], -off);
+          const float g = sc[ns] * (acc[ms][ns][j] - off);
+          const float u = sc[ns + 2] * (acc[ms][ns + 2][j] - off);
           const int64_t c = wrow[ns];
-          const int64_t pc = I4 ? (c & ~7) | ((c & 4) ? 2 * (c & 3) + 1 : 2 * (c & 3)) : c;
-          hrow[pc] = f32_to_bf16_bits(g / (1.0f + expf(-g)) * u);
+          const int64_t pc = I4 ? (c & ~7) | ((c & 1) ? 4 + ((c & 7) >> 1) : (c & 7) >> 1) : c;
+          const float hv = g / (1.0f + expf(-g)) * u;
+          hrow[pc] = f32_to_bf16_bits(hv);
+          if (prow) prow[orow * rows + c] = hv;
         }
       }
     }
@@ -461,7 +444,7 @@ __global__ __launch_bounds__(256) void k_make_tiles(const int32_t* __restrict__ 
 }
 
 // Row sums (fp32) of bf16 rows, one wave per row; with perm, also a copy of
-// the rows with every group of 8 stored in the order 0,4,1,5,2,6,3,7 (the
+// the rows with every group of 8 stored in the order 0,2,4,6,1,3,5,7 (the
 // activation order int4 tiles read).
 __global__ __launch_bounds__(256) void k_rowsum_bf16(const uint16_t* __restrict__ rows, int32_t n,
                                                      int32_t K, float* __restrict__ out,
@@ -473,7 +456,7 @@ __global__ __launch_bounds__(256) void k_rowsum_bf16(const uint16_t* __restrict_
   float s = 0.f;
   for (int c = lane * 8; c < K; c += 512) {
     const u32x4g v = *reinterpret_cast<const u32x4g*>(p + c);
-    if (perm) *reinterpret_cast<u32x4g*>(perm + r * K + c) = perm_0415(v);
+    if (perm) *reinterpret_cast<u32x4g*>(perm + r * K + c) = perm_0246(v);
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) s += __uint_as_float(w[d] << 16) + __uint_as_float(w[d] & 0xFFFF0000u);

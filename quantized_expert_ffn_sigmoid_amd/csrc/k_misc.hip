@@ -1,6 +1,7 @@
 // k_misc.hip -- weighted combine of the routed experts plus the shared expert,
 // and the dequantization test hook (gfx950).
 #include "moe_internal.h"
+#include "unpack.h"
 
 namespace moe {
 
@@ -58,7 +59,11 @@ hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* 
 }
 
 // Dequantized weights: out[r][c] = float(q) * scale[row0 + r] (one rounded
-// fp32 multiply); out_bf16 = bf16 bits of q (exact for |q| <= 256).
+// fp32 multiply); out_bf16 = bf16 bits of q (exact for |q| <= 256).  The codes
+// go through the kernels' own unpacking (unpack.h): q comes from the operand
+// the fp32 (GEMV) kernels read, (q + off) * 2^-9 for int4 and int2, (q + 8) /
+// 512 for int8, and for int4 the bf16 code from the matrix-core operand
+// q + 8; removing the offsets is exact.
 __global__ __launch_bounds__(256) void k_dequant(int dtype, const uint8_t* __restrict__ codes,
                                                  const float* __restrict__ scales, int32_t cols,
                                                  int32_t row0, int32_t n_rows,
@@ -73,18 +78,45 @@ __global__ __launch_bounds__(256) void k_dequant(int dtype, const uint8_t* __res
       out[i] = bf16_bits_to_f32(b);
       continue;
     }
-    int q;
+    float q;
+    float qb = 0.f;   // int4: the code from the matrix-core operand
     if (dtype == MOE_I4) {
-      const uint32_t v = (codes[r * (cols / 2) + c / 2] >> (4 * (c & 1))) & 0xFu;
-      q = (int)(v ^ 8u) - 8;
+      // the dword holding elements 8 (c / 8) .. + 7 (rows are whole bytes;
+      // the dword is read bytewise, as a row need not be 4-byte aligned)
+      const int64_t b0 = r * (cols / 2) + (c / 8) * 4;
+      const int64_t rb = r * (cols / 2) + cols / 2;
+      uint32_t w = 0;
+      for (int k = 0; k < 4; ++k)
+        if (b0 + k < rb) w |= (uint32_t)codes[b0 + k] << (8 * k);
+      const int e = (int)(c & 7);
+      float ql[4], qh[4];
+      i4_unpack_f32(w, ql, qh);
+      q = fmaf((e & 1) ? qh[e >> 1] : ql[e >> 1], 512.0f, -8.0f);
+      const u32x4u ob = i4_to_bf16(w);
+      // registers hold codes (0, 2), (4, 6), (1, 3), (5, 7)
+      const uint32_t reg = (e & 1) ? ((e >> 2) ? ob.w : ob.z) : ((e >> 2) ? ob.y : ob.x);
+      const int half = (e >> 1) & 1;
+      qb = bf16_bits_to_f32(half ? reg >> 16 : reg & 0xFFFFu) - 8.0f;
     } else if (dtype == MOE_I2) {
-      const uint32_t v = (codes[r * (cols / 4) + c / 4] >> (2 * (c & 3))) & 0x3u;
-      q = (int)(v ^ 2u) - 2;
+      const int64_t b0 = r * (cols / 4) + (c / 16) * 4;
+      const int64_t rb = r * (cols / 4) + cols / 4;
+      uint32_t w = 0;
+      for (int k = 0; k < 4; ++k)
+        if (b0 + k < rb) w |= (uint32_t)codes[b0 + k] << (8 * k);
+      const int e = (int)(c & 15);
+      float v[4];
+      i2_unpack_f32(w, e & 3, v);
+      q = fmaf(v[e >> 2], 512.0f, -2.0f);
     } else {
-      q = (int)(int8_t)codes[r * (int64_t)cols + c];
+      const int64_t b0 = r * (int64_t)cols + (c / 4) * 4;
+      const int64_t rb = r * (int64_t)cols + cols;
+      uint32_t w = 0;
+      for (int k = 0; k < 4; ++k)
+        if (b0 + k < rb) w |= (uint32_t)codes[b0 + k] << (8 * k);
+      q = fmaf(i8_unpack_f32(w, (int)(c & 3)), 512.0f, -8.0f);
     }
-    out[i] = __fmul_rn((float)q, scales[r]);
-    if (out_bf16) out_bf16[i] = f32_to_bf16_bits((float)q);
+    out[i] = __fmul_rn(q, scales[r]);
+    if (out_bf16) out_bf16[i] = f32_to_bf16_bits(dtype == MOE_I4 ? qb : q);
   }
 }
 

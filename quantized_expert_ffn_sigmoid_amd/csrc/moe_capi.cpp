@@ -241,6 +241,9 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   g.y_s = S;
   g.in_sliced = gu_ring;
   g.out_sliced = gu_ring && dn_ring;
+  float* hp = opts ? opts->h_f32 : nullptr;
+  g.hp = hp;
+  g.hp_s = hp ? hp + (int64_t)T * K * I : nullptr;
 
   if (pre) {
     record(opts, MOE_STAGE_ROUTE, 0, s);
@@ -338,6 +341,8 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     q.h_s = static_cast<uint16_t*>(h_sh);
     q.y = Y;
     q.y_s = S;
+    q.hp = g.hp;
+    q.hp_s = g.hp_s;
     float* rs = at<float>(ws, c.rs);
     q.rs_x = rs;
     q.rs_h = rs + T;

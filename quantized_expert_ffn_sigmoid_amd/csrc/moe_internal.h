@@ -155,6 +155,10 @@ struct GemvArgs {
   int32_t in_sliced, out_sliced;
   float* y;                // routed down output rows [slot f][H]
   float* y_s;              // shared down output rows [token][H]
+  // optional copies of h (gate/up) in fp32 before any rounding, rows as h and
+  // h_s, columns in natural order (a test hook; null: none)
+  float* hp;
+  float* hp_s;
   // filled in by the launcher
   MatGeo geo, geo_s;
   int32_t rb, nb, rb_s, nb_s;
@@ -187,6 +191,10 @@ struct GgArgs {
   uint16_t* h_s;             // [T][Is] bf16
   float* y;                  // [slot f][H]
   float* y_s;                // [T][H]
+  // optional fp32 copies of h and h_s before rounding, natural column order
+  // (a test hook; null: none)
+  float* hp;
+  float* hp_s;
   // fp32 row sums of the bf16 activation rows of int4 experts (the int4
   // operand carries an offset that the epilogue removes with them)
   const float* rs_x;         // [T]       rows of x

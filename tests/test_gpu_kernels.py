@@ -75,6 +75,33 @@ def test_dequant_bit_exact(dtype):
             assert np.array_equal(ob.cpu().numpy().ravel(), want)
 
 
+@pytest.mark.parametrize("dtype", [gen.I4, gen.I2, gen.I8])
+def test_dequant_every_code(dtype):
+    """Every byte value through the kernels' unpacking: rows of 256 bytes
+    holding 0..255 (int4: every pair of codes in [-8, 7]; int2: every four
+    codes in [-2, 1]; int8: every code in [-128, 127]), each byte in every
+    position of its dword across the rows, under scales of several binades
+    and a zero scale."""
+    per = {gen.I4: 2, gen.I2: 4, gen.I8: 1}[dtype]
+    cols = 256 * per
+    rows = 8
+    codes = np.stack([np.roll(np.arange(256, dtype=np.uint8), r) for r in range(rows)])
+    scales = np.array([1.0, 0.0137, 3.5e-3, 2.0 ** -20, 7.25, 0.0, 1e-30, 1.3e5], np.float32)
+    cd = torch.from_numpy(codes).to(DEV)
+    sd = torch.from_numpy(scales).to(DEV)
+    print_case("dequant every code", dtype)
+    out = torch.empty((rows, cols), dtype=torch.float32, device=DEV)
+    ob = torch.empty((rows, cols), dtype=torch.int16, device=DEV)
+    capi.moe_dequant_rows(dtype, cd, sd, cols, 0, rows, out, ob)
+    ref = oracle.dequant_rows(dtype, codes, scales, cols, 0, rows)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+    q = oracle.decode_codes(dtype, codes, rows * cols)
+    lo, hi = {gen.I4: (-8, 7), gen.I2: (-2, 1), gen.I8: (-128, 127)}[dtype]
+    assert q.min() == lo and q.max() == hi and len(np.unique(q)) == hi - lo + 1
+    want = gen.f32_to_bf16_bits(q.astype(np.float32)).view(np.int16)
+    assert np.array_equal(ob.cpu().numpy().ravel(), want)
+
+
 def _desc(cfg, dtype=None):
     spec = type("S", (), {})()
     for k in ("hidden", "inter", "n_experts", "top_k", "router", "n_group", "topk_group",

@@ -76,9 +76,36 @@ def test_layer_zero_input_and_determinism():
     assert np.array_equal(a, b) and np.array_equal(ia, ib) and np.array_equal(wa, wb)
 
 
+def _c3_sample(idx, n_experts, tile=64):
+    """Tokens that cover the grouped GEMM's tiles: the first, middle and last
+    rows of the first, middle and last (ragged) m-tiles of the 8 largest
+    buckets, the first and last rows of buckets that fill one tile of at most
+    16 or of 17-32 rows (the tiles that compute one or two 16-row subtiles),
+    and the first and last tokens of the batch."""
+    T, K = idx.shape
+    b = oracle.bucket(idx, n_experts)
+    counts, offsets, entries = b["counts"], b["offsets"], b["entries"]
+    tok = lambda p: int(entries[p]) // K
+    pick = {0, 1, T - 2, T - 1}
+    for e in np.argsort(-counts, kind="stable")[:8]:
+        n, p0 = int(counts[e]), int(offsets[e])
+        nt = (n + tile - 1) // tile
+        for m in sorted({0, nt // 2, nt - 1}):
+            rows = min(tile, n - m * tile)
+            for r in sorted({0, rows // 2, rows - 1}):
+                pick.add(tok(p0 + m * tile + r))
+    for lo, hi in ((1, 16), (17, 32)):
+        small = [e for e in np.nonzero((counts >= lo) & (counts <= hi))[0]][:24]
+        for e in small:
+            pick.add(tok(int(offsets[e])))
+            pick.add(tok(int(offsets[e + 1]) - 1))
+    return np.array(sorted(pick))
+
+
 def test_layer_c3_prefill_sampled():
     """GLM-scale batch-union prefill: 2048 bf16 tokens, Zipf-skewed routing.
-    All 2048 x 8 routing decisions are compared; outputs on sampled tokens."""
+    All 2048 x 8 routing decisions are compared; outputs on at least 128
+    tokens chosen to cover every kind of grouped-GEMM tile."""
     cfg = gen.get_config("c3")
     print_case("c3 prefill", cfg.batches[0])
     layer = gdev.generate_device_layer(cfg, 0, DEV)
@@ -89,7 +116,9 @@ def test_layer_c3_prefill_sampled():
     ridx, rw, _ = oracle.route(oracle.Desc.from_config(cfg), hl.w_router, hl.bias, x, T)
     assert np.array_equal(idx, ridx)
     assert np.allclose(w, rw, rtol=1e-6, atol=0)
-    sample = np.array([0, 1, 777, 1500, T - 2, T - 1])
+    sample = _c3_sample(ridx, cfg.n_experts)
+    print(f"  {len(sample)} tokens compared")
+    assert len(sample) >= 128
     ref, sidx, _ = oracle.layer_forward_host(hl, np.ascontiguousarray(x[sample]))
     assert np.array_equal(sidx, ridx[sample])
     band = oracle.layer_band_host(hl, np.ascontiguousarray(x[sample]), BF16_WINDOW)
@@ -253,3 +282,46 @@ def test_layer_top_p(name, T, p):
     assert np.allclose(w, rw, rtol=1e-6, atol=0)
     r = assert_close(out, ref, cfg.act_dtype == gen.BF16, f"layer top-p {name} T={T}")
     print(f"  max|err|/rms = {r:.3e}, experts kept {int((idx >= 0).sum())} of {idx.size}")
+
+
+# Codes over each container's whole range (int4 [-8, 7], int2 [-2, 1], int8
+# [-128, 127]) through every unpacking path: the GEMV's LDS ring (rows of at
+# least 64 granules: H and I of 2048), its register path (rows of 16 and 8
+# granules: H 512, I 256), the decode launches that carry the router
+# (shared expert of the same format), and the grouped GEMM (bf16
+# activations, more tokens than a decode batch).
+FULL_CASES = [
+    ("ring", gen.I4, 1), ("ring", gen.I4, 3), ("ring", gen.I2, 2), ("ring", gen.I8, 2),
+    ("regs", gen.I4, 2), ("regs", gen.I2, 3), ("regs", gen.I8, 1),
+    ("gemm", gen.I4, 150),
+]
+
+
+@pytest.mark.parametrize("path,dtype,T", FULL_CASES)
+def test_layer_full_code_range(path, dtype, T):
+    base = gen.get_config("c2")
+    small = dict(n_experts=16, top_k=4, n_group=4, topk_group=2, bias="normal",
+                 full_codes=True, seed=71, expert_dtype=dtype, shared_dtype=dtype)
+    if path == "ring":
+        cfg = gen.shrink(base, hidden=2048, inter=2048, **small)
+    elif path == "regs":
+        cfg = gen.shrink(base, hidden=512, inter=256, **small)
+    else:
+        cfg = gen.shrink(gen.get_config("c3"), hidden=512, inter=256, **small)
+    print_case("full code range", path, dtype, T)
+    hl = gen.host_layer(cfg, 0, experts="all")
+    q = oracle.decode_codes(dtype, hl.get(0)["gate_up"], 2 * cfg.inter * cfg.hidden)
+    assert q.min() == {gen.I4: -8, gen.I2: -2, gen.I8: -128}[dtype]
+    layer = gdev.upload_host_layer(hl, DEV)
+    x = gen.x_tokens(cfg, T, batch_id=700 + T)
+    out, idx, w = _layer_gpu(layer, x)
+    ref, ridx, rw = oracle.layer_forward_host(hl, x)
+    assert np.array_equal(idx, ridx)
+    assert np.allclose(w, rw, rtol=1e-6, atol=0)
+    if cfg.act_dtype == gen.BF16:
+        band = oracle.layer_band_host(hl, x, BF16_WINDOW)
+        r, b = assert_close_band(out, ref, band, f"full codes {path} {dtype} T={T}")
+        print(f"  max|err|/rms = {r:.3e}, max band/rms = {b:.3e}")
+    else:
+        r = assert_close(out, ref, False, f"full codes {path} {dtype} T={T}")
+        print(f"  max|err|/rms = {r:.3e}")

@@ -41,6 +41,36 @@ def test_hand_example(golden_dir, dtype):
     assert y[0].tolist() == g["y"]
 
 
+@pytest.mark.parametrize("dtype", [oracle.I4, oracle.BF16])
+def test_hand_example_h(golden_dir, dtype):
+    """The SwiGLU output before rounding, on the hand example: h = (logistic(1), 0)."""
+    g = json.load(open(os.path.join(golden_dir, "ffn_hand_example.json")))
+    d = oracle.Desc(hidden=g["hidden"], inter=g["inter"], n_experts=1, top_k=1, expert_dtype=dtype)
+    es = oracle.ExpertSet(dtype, [_hand_expert(g, dtype)])
+    x = np.array([g["x"]], np.float32)
+    assert oracle.expert_h(d, es, 0, x, n_rows=1)[0].tolist() == g["h"]
+
+
+def test_expert_h_matches_a_dense_swiglu():
+    """expert_h on a random int4 expert equals silu(G x) * (U x) from the
+    decoded codes and scales (numpy, fp64), and with f32 activations the
+    expert's output is the down matrix applied to that h."""
+    cfg = gen.shrink(gen.get_config("c0"), seed=12)
+    ex = gen.expert(cfg, 0, 3)
+    H, I = cfg.hidden, cfg.inter
+    d = oracle.Desc(hidden=H, inter=I, n_experts=1, top_k=1, expert_dtype=oracle.I4)
+    es = oracle.ExpertSet(oracle.I4, [ex])
+    x = gen.x_tokens(cfg, 3, batch_id=2)
+    h = oracle.expert_h(d, es, 0, x, n_rows=3)
+    gu = _np_codes(ex["gate_up"], H, oracle.I4) * ex["gate_up_scale"].astype(np.float64)[:, None]
+    dn = _np_codes(ex["down"], I, oracle.I4) * ex["down_scale"].astype(np.float64)[:, None]
+    xv = x.astype(np.float64)
+    g, u = xv @ gu[:I].T, xv @ gu[I:].T
+    np.testing.assert_allclose(h, g * expit(g) * u, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.expert_ffn(d, es, 0, x, n_rows=3), h @ dn.T, rtol=1e-12,
+                               atol=1e-14)
+
+
 def test_hand_example_bf16_activation(golden_dir):
     """With bf16 activations h is rounded to bf16: logistic(1) -> 0.73046875."""
     g = json.load(open(os.path.join(golden_dir, "ffn_hand_example.json")))

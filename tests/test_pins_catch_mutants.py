@@ -33,13 +33,19 @@ MUTANTS = {
     "silu_sign": ("double h = g / (1.0 + exp(-g)) * u;", "double h = g / (1.0 + exp(g)) * u;"),
     "gate_up_swapped": ("double h = g / (1.0 + exp(-g)) * u;", "double h = u / (1.0 + exp(-u)) * g;"),
     "down_transposed": ("acc += weight_at(dtype, dn, dns, I, o, r) * hbuf[r];", "acc += weight_at(dtype, dn, dns, I, r % H, o % I) * hbuf[r];"),
-    "no_bf16_h_rounding": ("if (act_bf16) h = bf16_to_double(float_to_bf16((float)h));", ""),
+    "no_bf16_h_rounding": ("hbuf[r] = bf16_to_double(float_to_bf16((float)hbuf[r]));", "hbuf[r] = hbuf[r];"),
     "shared_dropped": ("for (int64_t o = 0; o < H && rc == ORC_OK; ++o) out[t * H + o] += S[o];", ""),
     "combine_weight_order": ("acc += w64[t * K + j] * Y[(t * K + j) * H + o];", "acc += w64[t * K + (K - 1 - j)] * Y[(t * K + j) * H + o];"),
     "bucket_unstable": ("entries[fill[e]] = (int32_t)f;", "entries[offsets[e + 1] - 1 - (fill[e] - offsets[e])] = (int32_t)f;"),
     "logit_drop_last": ("for (int64_t h = 0; h < H; ++h)\n      acc += x_at", "for (int64_t h = 0; h < H - 1; ++h)\n      acc += x_at"),
     "rmsnorm_no_eps": ("double den = sqrt(ss / (double)hidden + eps);", "double den = sqrt(ss / (double)hidden);"),
     "softmax_wrong_ref": ("wk[j] = exp(z[idx[j]] - z0);", "wk[j] = exp(z[idx[j]] - z0) * (j + 1);"),
+    "band_distance_from_lo": ("const double mid = 0.5 * ((double)lo + (double)hi);", "const double mid = (double)lo;"),
+    "band_absolute_window": ("if (fabs((double)hf - mid) <= window * eb[r])", "if (fabs((double)hf - mid) <= window)"),
+    "band_relative_window": ("if (fabs((double)hf - mid) <= window * eb[r])", "if (fabs((double)hf - mid) <= window * fabs((double)hf))"),
+    "band_one_sided": ("if (fabs((double)hf - mid) <= window * eb[r])", "if ((double)hf - mid >= 0.0 && (double)hf - mid <= window * eb[r])"),
+    "band_scale_drops_gate_term": ("ebuf[r] = fabs(dsilu * u) * ag + fabs(g * sg) * au;", "ebuf[r] = fabs(g * sg) * au;"),
+    "band_scale_wrong_derivative": ("const double dsilu = sg * (1.0 + g * (1.0 - sg));", "const double dsilu = sg;"),
     "scale_of_wrong_row": ("return (double)code_at(dtype, row, c) * (double)scale[r];", "return (double)code_at(dtype, row, c) * (double)scale[r ^ 1];"),
 }
 
