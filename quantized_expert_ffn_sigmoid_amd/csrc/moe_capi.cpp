@@ -8,6 +8,7 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "down_fused.h"
 #include "moe.h"
 #include "moe_internal.h"
 
@@ -206,6 +207,26 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   // leading blocks (the shared expert does not depend on the routing), and
   // the routed launches follow.  The shared gate/up then reads x as it is.
   const bool pre = !use_gg && fused_route && gu_ring && dn_ring && gemv_pre_supported(d, Ish);
+  // one token on the ring kernels: the down projections (routed and shared)
+  // and the combine run as one launch that writes out directly
+  const bool fused_dn = !use_gg && T == 1 && gu_ring && dn_ring && down_fused_supported(d, T);
+  DownFusedArgs fa{};
+  if (fused_dn) {
+    fa.w = dev_set(w.routed);
+    if (has_sh) fa.ws = dev_set(w.shared);
+    fa.has_shared = has_sh;
+    fa.H = H;
+    fa.I = I;
+    fa.Is = Ish;
+    fa.slot_tab = tb.slot_tab;
+    fa.n_slots = tb.n_tab;
+    fa.topk_w = tw;
+    fa.h = h;
+    fa.h_s = h_sh;
+    fa.residual = residual;
+    fa.out = out;
+    fa.y_copy = y_copy;
+  }
   SliceReq sr{};
   if (gu_ring && !use_gg) {
     sr.epg_a = epg_r;
@@ -263,6 +284,25 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     p.z = z;
     p.sr = sr;
     MOE_TRY(launch_gemv_pre(gs, p, false, d.shared_dtype, act_bf16, s));
+    if (fused_dn) {
+      // selection and grouping, one block; the shared down projection joins
+      // the routed ones in the fused launch
+      MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
+                                   active, n_active, s, tb));
+      record(opts, MOE_STAGE_ROUTE, 1, s);
+      record(opts, MOE_STAGE_BUCKET, 0, s);
+      record(opts, MOE_STAGE_BUCKET, 1, s);
+      g.has_shared = 0;
+      record(opts, MOE_STAGE_GATE_UP, 0, s);
+      MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
+      record(opts, MOE_STAGE_GATE_UP, 1, s);
+      record(opts, MOE_STAGE_DOWN, 0, s);
+      MOE_TRY(launch_down_fused(d, fa, act_bf16, s));
+      record(opts, MOE_STAGE_DOWN, 1, s);
+      record(opts, MOE_STAGE_COMBINE, 0, s);
+      record(opts, MOE_STAGE_COMBINE, 1, s);
+      return MOE_OK;
+    }
     gs.in_sliced = g.out_sliced;
     p = PreArgs{};
     p.kind = kPreSelect;
@@ -371,6 +411,14 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_GATE_UP, 1, s);
 
+  if (fused_dn) {
+    record(opts, MOE_STAGE_DOWN, 0, s);
+    MOE_TRY(launch_down_fused(d, fa, act_bf16, s));
+    record(opts, MOE_STAGE_DOWN, 1, s);
+    record(opts, MOE_STAGE_COMBINE, 0, s);
+    record(opts, MOE_STAGE_COMBINE, 1, s);
+    return MOE_OK;
+  }
   record(opts, MOE_STAGE_DOWN, 0, s);
   g.in_sliced = g.out_sliced;
   MOE_TRY(launch_gemv(g, true, d.expert_dtype, d.shared_dtype, act_bf16, T, s));

@@ -262,6 +262,13 @@ hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);
 
+// One-token decode: the routed and shared down projections and the combine
+// in one launch (k_down_fused.hip); whether the layer's shapes are covered.
+struct DownFusedArgs;
+bool down_fused_supported(const moe_layer_desc& d, int32_t T);
+hipError_t launch_down_fused(const moe_layer_desc& d, DownFusedArgs a, int act_bf16,
+                             hipStream_t s);
+
 // Grouped GEMM: whether a layer qualifies, the routed m-tile bound for T
 // tokens, the tile list from the buckets, and the launch.
 bool ggemm_supported(const moe_layer_desc& d);
