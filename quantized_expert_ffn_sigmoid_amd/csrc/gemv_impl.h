@@ -1054,6 +1054,13 @@ hipError_t gemv_go(const GemvArgs& a, int ntmax, int act_bf16, unsigned blocks, 
   return hipGetLastError();
 }
 
+// Geometry, token mode and block sizes of a GEMV launch (k_gemv.hip); returns
+// the number of blocks (0: no work) or -1 when a shape is not covered.
+// ntmax: tokens one pass of a block takes; target_blocks: blocks of one
+// resident round (2048 waves of 4-wave blocks).
+long long plan_gemv(GemvArgs& a, bool down, int dtype, int& shared_dtype, int max_rows_per_slot,
+                    bool allow_nt2, int& ntmax, int64_t target_blocks = 512);
+
 // Per-format entry points (one translation unit each, compiled in parallel).
 // The shared expert's slice length always equals the routed one (both K/64,
 // or the same short-row geometry), so only its format varies.

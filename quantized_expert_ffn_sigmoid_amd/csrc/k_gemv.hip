@@ -93,9 +93,8 @@ constexpr int64_t kMinBytesPerWave = 8 * 1024;
 // Fills in the geometry, token mode and block sizes of a launch; returns the
 // number of GEMV blocks (0: no work) or -1 when a shape is not covered.
 // ntmax: tokens one pass of a block takes (1, or 2 where allowed).
-static long long plan_gemv(GemvArgs& a, bool down, int dtype, int& shared_dtype,
-                           int max_rows_per_slot, bool allow_nt2, int& ntmax,
-                           int64_t target_blocks = kTargetBlocks) {
+long long plan_gemv(GemvArgs& a, bool down, int dtype, int& shared_dtype, int max_rows_per_slot,
+                    bool allow_nt2, int& ntmax, int64_t target_blocks) {
   const int kin = down ? a.I : a.H, kin_s = down ? a.Is : a.H;
   const int rows = down ? a.H : a.I, rows_s = down ? a.H : a.Is;
   if (!make_geo(dtype, kin, a.geo)) return -1;
@@ -151,7 +150,8 @@ static long long plan_gemv(GemvArgs& a, bool down, int dtype, int& shared_dtype,
 hipError_t launch_gemv(GemvArgs a, bool down, int dtype, int shared_dtype, int act_bf16,
                        int max_rows_per_slot, hipStream_t s) {
   int ntmax = 1;
-  const long long blocks = plan_gemv(a, down, dtype, shared_dtype, max_rows_per_slot, true, ntmax);
+  const long long blocks =
+      plan_gemv(a, down, dtype, shared_dtype, max_rows_per_slot, true, ntmax, kTargetBlocks);
   if (blocks < 0) return hipErrorInvalidValue;
   if (blocks == 0) return hipSuccess;
   const unsigned nblk = (unsigned)blocks;

@@ -266,6 +266,28 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   g.hp = hp;
   g.hp_s = hp ? hp + (int64_t)T * K * I : nullptr;
 
+  // One token with the fused down launch: the routed gate/up blocks run the
+  // selection and grouping themselves (no launch of its own).
+  // (outside the decode launches that carry the router, a shared expert's
+  // gate/up shares the routed launch, which this variant does not hold)
+  const bool sel_inline = fused_dn && (pre || !has_sh) && gemv_sel_supported(d, T);
+  PreArgs sel{};
+  if (sel_inline) {
+    sel.sp = select_params(d);
+    sel.T = T;
+    sel.zin = z;
+    sel.bias = w.bias;
+    sel.idx = idx;
+    sel.w = tw;
+    sel.counts = counts;
+    sel.offsets = offsets;
+    sel.entries = entries;
+    sel.inverse = inverse;
+    sel.active = active;
+    sel.n_active = n_active;
+    sel.tb = tb;
+  }
+
   if (pre) {
     record(opts, MOE_STAGE_ROUTE, 0, s);
     GemvArgs gs = g;
@@ -285,16 +307,21 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     p.sr = sr;
     MOE_TRY(launch_gemv_pre(gs, p, false, d.shared_dtype, act_bf16, s));
     if (fused_dn) {
-      // selection and grouping, one block; the shared down projection joins
-      // the routed ones in the fused launch
-      MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
-                                   active, n_active, s, tb));
+      // the shared down projection joins the routed ones in the fused launch;
+      // the selection and grouping run in the routed gate/up blocks (or, for
+      // shapes that launch does not compile, in one block of their own)
+      if (!sel_inline)
+        MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
+                                     active, n_active, s, tb));
       record(opts, MOE_STAGE_ROUTE, 1, s);
       record(opts, MOE_STAGE_BUCKET, 0, s);
       record(opts, MOE_STAGE_BUCKET, 1, s);
       g.has_shared = 0;
       record(opts, MOE_STAGE_GATE_UP, 0, s);
-      MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
+      if (sel_inline)
+        MOE_TRY(launch_gemv_sel(g, sel, d.expert_dtype, act_bf16, s));
+      else
+        MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
       record(opts, MOE_STAGE_GATE_UP, 1, s);
       record(opts, MOE_STAGE_DOWN, 0, s);
       MOE_TRY(launch_down_fused(d, fa, act_bf16, s));
@@ -343,10 +370,10 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   // the down projections
   MOE_TRY(launch_router_logits(w.w_router, x, act_bf16, T, H, E, z, sr, s,
                                reinterpret_cast<double*>(Y), (int64_t)T * K * H / 2));
-  if (fused_route)
+  if (fused_route && !sel_inline)
     MOE_TRY(launch_select_bucket(d, z, w.bias, T, idx, tw, counts, offsets, entries, inverse,
                                  active, n_active, s, tb));
-  else
+  else if (!fused_route)
     MOE_TRY(launch_router_select(d, z, w.bias, T, idx, tw, s));
   record(opts, MOE_STAGE_ROUTE, 1, s);
 
@@ -408,7 +435,10 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   }
 
   record(opts, MOE_STAGE_GATE_UP, 0, s);
-  MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
+  if (sel_inline)
+    MOE_TRY(launch_gemv_sel(g, sel, d.expert_dtype, act_bf16, s));
+  else
+    MOE_TRY(launch_gemv(g, false, d.expert_dtype, d.shared_dtype, act_bf16, T, s));
   record(opts, MOE_STAGE_GATE_UP, 1, s);
 
   if (fused_dn) {

@@ -262,6 +262,13 @@ hipError_t launch_dequant(int dtype, const void* codes, const float* scales, int
                           int32_t row0, int32_t n_rows, float* out, uint16_t* out_bf16,
                           hipStream_t s);
 
+// One-token decode: the routed gate/up launch whose blocks each run the
+// selection and grouping themselves (k_gemv_sel.hip), block 0 writing them
+// out (p: the selection parameters, logits and outputs, as for the selection
+// launch); whether the layer's shapes are compiled.
+bool gemv_sel_supported(const moe_layer_desc& d, int32_t T);
+hipError_t launch_gemv_sel(GemvArgs a, const PreArgs& p, int dtype, int act_bf16, hipStream_t s);
+
 // One-token decode: the routed and shared down projections and the combine
 // in one launch (k_down_fused.hip); whether the layer's shapes are covered.
 struct DownFusedArgs;
