@@ -39,6 +39,19 @@ __device__ __forceinline__ double dpp_d(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// fp64 maximum and minimum as single instructions (the library fmax/fmin
+// also canonicalize their operands; the values here are never NaN).
+__device__ __forceinline__ double dmax(double a, double b) {
+  double r;
+  asm("v_max_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ double dmin(double a, double b) {
+  double r;
+  asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ double readlane_d(double v, int lane) {
   const long long b = __double_as_longlong(v);
   const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), lane);
@@ -96,21 +109,57 @@ __device__ __forceinline__ double swap_max(double v, bool halves) {
   }
   const double a = __longlong_as_double(((long long)hi2 << 32) | lo2);
   const double c = __longlong_as_double(((long long)hi3 << 32) | lo3);
-  return fmax(a, c);
+  return dmax(a, c);
 }
 __device__ __forceinline__ double wave_max_d(double v) {
-  v = fmax(v, dpp_d<kDppXor1>(v));
-  v = fmax(v, dpp_d<kDppXor2>(v));
-  v = fmax(v, dpp_d<kDppHalfMirror>(v));
-  v = fmax(v, dpp_d<kDppMirror>(v));
+  v = dmax(v, dpp_d<kDppXor1>(v));
+  v = dmax(v, dpp_d<kDppXor2>(v));
+  v = dmax(v, dpp_d<kDppHalfMirror>(v));
+  v = dmax(v, dpp_d<kDppMirror>(v));
   v = swap_max(v, false);
   return swap_max(v, true);
 }
 
+// Order-preserving 64-bit keys of doubles: key(a) > key(b) exactly when
+// a > b (finite values; -0 below +0, which the selection never compares).
+__device__ __forceinline__ uint64_t order_key(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double key_value(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __longlong_as_double((long long)b);
+}
+
+// Wave-wide maximum of 32-bit unsigned values, in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  const auto p16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(p16[0], p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(p32[0], p32[1]);
+}
+
+// Wave-wide maximum of 64-bit keys, in every lane: the high words first, then
+// the low words of the lanes that hold the largest high word.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)k : 0u);
+  return ((uint64_t)mh << 32) | ml;
+}
+
 // Two largest values (a >= b) merged with a partner's pair.
 __device__ __forceinline__ void top2_merge(double& a, double& b, double oa, double ob) {
-  const double hi = fmax(a, oa), lo = fmin(a, oa);
-  b = fmax(lo, fmax(b, ob));
+  const double hi = dmax(a, oa), lo = dmin(a, oa);
+  b = dmax(lo, dmax(b, ob));
   a = hi;
 }
 
@@ -172,8 +221,8 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
       double a = NEG, b = NEG;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
-        const double hi = fmax(a, c[i]), lo = fmin(a, c[i]);
-        b = fmax(b, lo);
+        const double hi = dmax(a, c[i]), lo = dmin(a, c[i]);
+        b = dmax(b, lo);
         a = hi;
       }
       segment_top2(a, b, lpg);
@@ -197,8 +246,8 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
         for (int i = 0; i < EPL; ++i) {
           const int e = lane * EPL + i;
           const double x = e / per == g ? c[i] : NEG;
-          const double hi = fmax(a, x), lo = fmin(a, x);
-          b = fmax(b, lo);
+          const double hi = dmax(a, x), lo = dmin(a, x);
+          b = dmax(b, lo);
           a = hi;
         }
         wave_top2(a, b);
@@ -220,42 +269,75 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     }
   }
 
-  // top-k among the open experts, in rank order; lane j keeps rank j's mass
-  // and the mass of the ranks before it (for adaptive top-p)
-  int my_idx = 0;
-  double my_s = 0.0, my_before = 0.0, ssum = 0.0, z0 = 0.0;
-  for (int j = 0; j < p.K; ++j) {
-    // the best open value, then the lowest expert holding it (ballots: the
-    // experts of slot i of each lane are i, EPL + i, 2 EPL + i, ...)
-    double m = c[0];
+  // top-k among the open experts, in rank order.  Each lane first orders its
+  // own candidates (value descending, then expert ascending: the swaps are
+  // strict, so equal values keep the ascending order); a round then takes
+  // the largest head over the lanes, and the lowest lane holding it holds
+  // the lowest expert with that value (lane l holds experts l*EPL ..
+  // l*EPL+EPL-1), which pops its head.  Lane j keeps rank j's expert and
+  // selection score.
+  uint64_t hk[EPL];
+  double hs[EPL];
+  int hx[EPL];
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) m = fmax(m, c[i]);
-    m = wave_max_d(m);
-    int ri = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const uint64_t b = __ballot(c[i] == m);
-      if (b) ri = min(ri, (int)__builtin_ctzll(b) * EPL + i);
-    }
-    const int owner = min(ri / EPL, kWave - 1), slot = ri % EPL;
-    double bs = sv[0];
-#pragma unroll
-    for (int i = 1; i < EPL; ++i) bs = slot == i ? sv[i] : bs;
-    const double s_win = readlane_d(bs, owner);
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) c[i] = lane * EPL + i == ri ? NEG : c[i];
-    double contrib;
-    if constexpr (SOFTMAX) {
-      if (j == 0) z0 = s_win;
-      contrib = exp(s_win - z0);
-    } else {
-      contrib = s_win;
-    }
-    my_before = lane == j ? ssum : my_before;
-    ssum += contrib;   // sequential sum in rank order
-    my_idx = lane == j ? ri : my_idx;
-    my_s = lane == j ? contrib : my_s;
+  for (int i = 0; i < EPL; ++i) {
+    hk[i] = order_key(c[i]);
+    hs[i] = sv[i];
+    hx[i] = lane * EPL + i;
   }
+#pragma unroll
+  for (int a = 1; a < EPL; ++a) {
+#pragma unroll
+    for (int b = a; b > 0; --b) {
+      const bool sw = hk[b] > hk[b - 1];
+      const uint64_t k0 = hk[b - 1];
+      const double s0 = hs[b - 1];
+      const int x0 = hx[b - 1];
+      hk[b - 1] = sw ? hk[b] : k0;
+      hs[b - 1] = sw ? hs[b] : s0;
+      hx[b - 1] = sw ? hx[b] : x0;
+      hk[b] = sw ? k0 : hk[b];
+      hs[b] = sw ? s0 : hs[b];
+      hx[b] = sw ? x0 : hx[b];
+    }
+  }
+  int my_idx = 0;
+  double my_raw = 0.0;
+  for (int j = 0; j < p.K; ++j) {
+    const uint64_t m = wave_max_key(hk[0]);
+    const uint64_t b = __ballot(hk[0] == m);
+    const int owner = (int)__builtin_ctzll(b);
+    const int ri = __builtin_amdgcn_readlane(hx[0], owner);
+    const double s_win = readlane_d(hs[0], owner);
+    if (lane == owner) {
+#pragma unroll
+      for (int i = 0; i + 1 < EPL; ++i) {
+        hk[i] = hk[i + 1];
+        hs[i] = hs[i + 1];
+        hx[i] = hx[i + 1];
+      }
+      hk[EPL - 1] = 0;   // below every key of a finite or -inf value
+    }
+    my_idx = lane == j ? ri : my_idx;
+    my_raw = lane == j ? s_win : my_raw;
+  }
+  // masses in rank order: the sigmoid values, or exp(z - z_max) for softmax
+  // (every lane its own rank's), summed sequentially in rank order; lane j
+  // keeps rank j's mass and the mass of the ranks before it (adaptive top-p)
+  double contrib;
+  if constexpr (SOFTMAX) {
+    const double z0 = readlane_d(my_raw, 0);
+    contrib = exp((lane < p.K ? my_raw : z0) - z0);
+  } else {
+    contrib = my_raw;
+  }
+  double ssum = 0.0, my_before = 0.0;
+  for (int j = 0; j < p.K; ++j) {
+    const double cj = readlane_d(contrib, j);
+    my_before = lane == j ? ssum : my_before;
+    ssum += cj;
+  }
+  const double my_s = contrib;
   // adaptive top-p: rank j stays when the mass before it is below top_p of
   // the total; the kept prefix's mass (the mass before the first dropped
   // rank) renormalizes the weights
