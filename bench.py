@@ -117,7 +117,7 @@ class Hip:
 # a digest of the sources that build and launch the kernel; once any of them
 # changes the counters no longer describe it and the traffic is reported null.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemv_gate_up__glm_layer_decode_1tok.md")
-TRAFFIC_SOURCES = ["gemv_impl.h", "route_device.h", "k_gemv.hip", "k_gemv_i4_gu.hip",
+TRAFFIC_SOURCES = ["gemv_impl.h", "route_device.h", "unpack.h", "k_gemv.hip", "k_gemv_sel.hip",
                    "moe_internal.h", "moe_capi.cpp"]
 
 
@@ -207,10 +207,18 @@ def layer_bytes(cfg, dtype, n_active, T):
 
 
 # ------------------------------------------------------------ CPU oracle
-def cpu_baseline(cfg, dtype, T, seconds, max_tokens=256):
-    """The oracle as it stands on a bounded sample of the same workload:
-    token batches of the workload, each on layer 0; only the oracle's layer
-    forward is timed (expert generation on the host is not)."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(cfg, dtype, T, seconds, max_tokens):
     import oracle
     d = oracle.Desc.from_config(cfg, expert_dtype=dtype)
     hl = gen.host_layer(cfg, 0, dtype=dtype)
@@ -228,9 +236,29 @@ def cpu_baseline(cfg, dtype, T, seconds, max_tokens=256):
         hl.experts.clear()
         if spent >= seconds:
             break
-    return dict(value=done / spent, unit="tokens/s", cores=oracle.max_threads(), kind="oracle",
+    return done / spent, done, b, spent
+
+
+def cpu_baseline(cfg, dtype, T, seconds, max_tokens=256):
+    """The oracle as it stands on a bounded sample of the same workload:
+    token batches of the workload, each on layer 0; only the oracle's layer
+    forward is timed (expert generation on the host is not).  Timed on all
+    the host threads the oracle uses, and on one."""
+    import oracle
+    cores = oracle.max_threads()
+    rate, done, b, spent = _oracle_rate(cfg, dtype, T, seconds, max_tokens)
+    oracle.set_threads(1)
+    try:
+        rate1, done1, b1, spent1 = _oracle_rate(cfg, dtype, T, seconds, max_tokens)
+    finally:
+        oracle.set_threads(cores)
+    return dict(value=rate, unit="tokens/s", cores=cores, kind="oracle",
                 sample=f"{done} tokens in {b} batches of {T} (layer 0 of the workload), "
-                       f"oracle layer forward timed for {spent:.1f} s")
+                       f"oracle layer forward timed for {spent:.1f} s",
+                one_thread={"value": rate1, "unit": "tokens/s", "cores": 1,
+                            "sample": f"{done1} tokens in {b1} batches of {T}, "
+                                      f"timed for {spent1:.1f} s"},
+                cpu_model=cpu_model())
 
 
 # -------------------------------------------------------- requantization
@@ -292,58 +320,26 @@ def bench_requant(args):
 
 
 # ------------------------------------------------------------------ main
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", default="c2",
-                    choices=["c2", "c2i8", "c4i4", "c4i2", "c3", "c1", "c0", "requant"])
-    ap.add_argument("--batch", type=int, default=None, help="tokens per step (c4: 2, 4 or 16)")
-    ap.add_argument("--layers", type=int, default=8, help="distinct layer instances rotated")
-    ap.add_argument("--eager", action="store_true", help="launch each step eagerly (no graph)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", action="store_true", help="also time every stage")
-    ap.add_argument("--top-p", type=float, default=0.0,
-                    help="adaptive expert top-p (0: off): the router keeps the shortest prefix "
-                         "of each token's top-k whose routing mass reaches this share")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy five times (the known-size kernel "
-                         "that scales the FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-    if args.copy_calibration:
-        import torch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
-                          "launches": 5}))
-        return
+def percentiles(v):
+    v = np.asarray(v, dtype=np.float64)
+    return {"median": round(float(np.median(v)), 3), "p10": round(float(np.percentile(v, 10)), 3),
+            "p90": round(float(np.percentile(v, 90)), 3)}
 
-    if args.workload == "requant":
-        return bench_requant(args)
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is a design "
-                                   "only (expert-parallel by router group), --gpus must be 1"}))
-        sys.exit(2)
-
+def run_workload(args, wl, K, W, with_cpu, replays=5, ab_lib=None):
+    """Build the workload's inputs in HBM, capture its steps into HIP graphs and
+    time them; returns the result dict (see the fields at the end)."""
     import torch
     from gen import device as gdev
     from quantized_expert_ffn_sigmoid_amd import capi
 
     dev = torch.device("cuda:0")
     hip = Hip()
-    wl = args.workload
     base = {"c2": "c2", "c2i8": "c2", "c4i4": "c4", "c4i2": "c4", "c3": "c3", "c1": "c1",
             "c0": "c0"}[wl]
     cfg = gen.get_config(base, top_p=args.top_p) if args.top_p else gen.get_config(base)
     dtype = {"c4i2": gen.I2, "c2i8": gen.I8}.get(wl, cfg.expert_dtype)
-    T = args.batch or (16 if base == "c4" else cfg.batches[0])
+    T = (args.batch if base == "c4" else None) or (16 if base == "c4" else cfg.batches[0])
     L = args.layers if base in ("c2", "c3", "c4") else 1
     if base == "c3":
         L = min(L, 2)
@@ -373,7 +369,7 @@ def main():
     # ---- unique experts per step (library routing, computed before timing)
     n_active = []
     kept_slots = []
-    for i in range(max(args.steps, 1)):
+    for i in range(max(K, 1)):
         l, p = i % L, i % P
         if i < P * L:
             capi.moe_route(desc, layers[l].w_router, layers[l].bias, xs[p], T, idx, tw, ws, nb)
@@ -383,8 +379,8 @@ def main():
         else:
             n_active.append(n_active[i % (P * L)])
 
-    K, W = args.steps, args.warmup
     stream = torch.cuda.Stream(device=dev)
+    sh = stream.cuda_stream
     stage_ids = list(range(capi.MOE_N_STAGES)) if args.stages else [capi.MOE_STAGE_GATE_UP]
     evs = [[[hip.event(), hip.event()] for _ in stage_ids] for _ in range(K)]
     # an empty event pair per step: what an event bracket adds by itself
@@ -398,17 +394,19 @@ def main():
         cap = not args.eager
         if timed:
             events = [0] * (2 * capi.MOE_N_STAGES)
-            for k, s in enumerate(stage_ids):
-                events[2 * s], events[2 * s + 1] = evs[i][k]
-            hip.record(evp[i][0], stream.cuda_stream, cap)
-            hip.record(evp[i][1], stream.cuda_stream, cap)
+            for k, s_id in enumerate(stage_ids):
+                events[2 * s_id], events[2 * s_id + 1] = evs[i][k]
+            hip.record(evp[i][0], sh, cap)
+            hip.record(evp[i][1], sh, cap)
         if whole:
-            hip.record(evw[i][0], stream.cuda_stream, cap)
+            hip.record(evw[i][0], sh, cap)
         capi.moe_layer_forward_ex(desc, weights[l], xs[p], T, out, None, None, ws, nb,
-                                  stream=stream.cuda_stream, events=events)
+                                  stream=sh, events=events)
         if whole:
-            hip.record(evw[i][1], stream.cuda_stream, cap)
+            hip.record(evw[i][1], sh, cap)
 
+    rep_ms = []
+    ab = None
     # The headline loop carries no event nodes; per-kernel durations come from a
     # second pass over the same K steps with events around the stages.
     if args.eager:
@@ -427,7 +425,6 @@ def main():
             step(i, False, whole=True)
         torch.cuda.synchronize()
     else:
-        sh = stream.cuda_stream
         step(0, False)                       # first launches outside any capture
         torch.cuda.synchronize()
         gw = hip.capture(sh, lambda: [step(i, False) for i in range(W)])
@@ -444,6 +441,17 @@ def main():
         torch.cuda.synchronize()
         hip.launch(gb, sh)
         torch.cuda.synchronize()
+        # further replays of the same K steps: the spread of the step time
+        r0, r1 = hip.event(), hip.event()
+        for _ in range(replays):
+            hip.record(r0, sh, False)
+            hip.launch(gt, sh)
+            hip.record(r1, sh, False)
+            torch.cuda.synchronize()
+            rep_ms.append(hip.elapsed_ms(r0, r1) / K)
+        if ab_lib:
+            ab = ab_compare(hip, capi, ab_lib, gt, sh, out, lambda: [step(i, False) for i in range(K)],
+                            K, replays)
 
     elapsed = t1 - t0
     ms_step = 1e3 * elapsed / K
@@ -459,7 +467,8 @@ def main():
     # then take several times their usual time.
     bracket_ms = float(np.median(stage_ms[capi.MOE_STAGE_GATE_UP]))
     pair_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evp]))
-    whole_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evw]))
+    whole = [hip.elapsed_ms(a, b) for a, b in evw]
+    whole_ms = float(np.median(whole))
     over_ms = whole_ms - ms_step
     gu_ms = bracket_ms - over_ms if 0.0 < over_ms < 0.5 * bracket_ms else bracket_ms
     gu_bytes = float(np.mean([gate_up_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
@@ -485,8 +494,11 @@ def main():
             "bracket_overhead_us": round(over_ms * 1e3, 3),
         }
     else:
+        sel = T == 1 and shared_runs_with_router(cfg, dtype, T)
         roofline = {
-            "kernel": ("moe::k_gemv gate/up + SwiGLU (routed experts)"
+            "kernel": ("moe::k_gemv_sel routed gate/up + SwiGLU (the selection in the same launch)"
+                       if sel else
+                       "moe::k_gemv gate/up + SwiGLU (routed experts)"
                        if shared_runs_with_router(cfg, dtype, T) else
                        "moe::k_gemv gate/up + SwiGLU (routed and shared experts)"),
             "bound": "hbm",
@@ -536,10 +548,125 @@ def main():
                     "unique_experts_per_step": round(float(np.mean(n_active[:K])), 2)},
         "roofline": roofline,
     }
+    # per-step time: over further replays of the K steps (each replay's mean),
+    # and over the steps of the bracketed replay (each step's bracket)
+    if rep_ms:
+        res["step_us"] = dict(replays=len(rep_ms), **percentiles(np.array(rep_ms) * 1e3))
+        res["step_us"]["per_step_bracket"] = percentiles(np.array(whole) * 1e3)
     if args.stages:
-        res["stage_us"] = {names[s]: round(1e3 * float(np.mean(v)), 3) for s, v in stage_ms.items()}
-    if not args.no_cpu_baseline:
+        res["stage_us"] = {names[s_id]: round(1e3 * float(np.mean(v)), 3)
+                           for s_id, v in stage_ms.items()}
+    if ab is not None:
+        res["ab"] = ab
+    if with_cpu:
         res["cpu_baseline"] = cpu_baseline(cfg, dtype, T, args.cpu_seconds)
+    del layers, ws, xs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def ab_compare(hip, capi, lib_b, graph_a, sh, out, capture_steps, K, pairs):
+    """ABBA comparison of the in-tree library (A) with another build of it (B,
+    the path given): B's steps are captured with B's library, the two graphs are
+    replayed in the order A B B A, `pairs` times, and the per-step times
+    compared.  Gated on the outputs: the last step's output after a replay of
+    A and of B must be the same bits (a variant that changes the result is not
+    an A/B of the same computation)."""
+    import hashlib
+    import torch
+    lib_a = capi.lib()
+    capi._lib = capi.load_library(lib_b)
+    try:
+        graph_b = hip.capture(sh, capture_steps)
+    finally:
+        capi._lib = lib_a
+    r0, r1 = hip.event(), hip.event()
+
+    def replay(g):
+        hip.record(r0, sh, False)
+        hip.launch(g, sh)
+        hip.record(r1, sh, False)
+        torch.cuda.synchronize()
+        return hip.elapsed_ms(r0, r1) / K, hashlib.sha256(out.cpu().numpy().tobytes()).hexdigest()
+
+    ta, tb, ha, hb = [], [], set(), set()
+    for _ in range(pairs):
+        for g, t, h in ((graph_a, ta, ha), (graph_b, tb, hb), (graph_b, tb, hb), (graph_a, ta, ha)):
+            ms, digest = replay(g)
+            t.append(ms)
+            h.add(digest)
+    ma, mb = float(np.median(ta)), float(np.median(tb))
+    return {"lib_b": lib_b, "order": "ABBA", "pairs": pairs,
+            "a_us": percentiles(np.array(ta) * 1e3), "b_us": percentiles(np.array(tb) * 1e3),
+            "b_over_a": round(mb / ma, 4), "outputs_identical": ha == hb and len(ha) == 1}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="c2",
+                    choices=["c2", "c2i8", "c4i4", "c4i2", "c3", "c1", "c0", "requant"])
+    ap.add_argument("--batch", type=int, default=None, help="tokens per step (c4: 2, 4 or 16)")
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer instances rotated")
+    ap.add_argument("--eager", action="store_true", help="launch each step eagerly (no graph)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill (c3) measurement the default workload also reports")
+    ap.add_argument("--replays", type=int, default=5,
+                    help="further replays of the timed steps for the spread of the step time")
+    ap.add_argument("--ab", default=None, metavar="LIBMOE_SO",
+                    help="also time another build of libmoe.so against the in-tree one, "
+                         "ABBA-interleaved, gated on identical outputs")
+    ap.add_argument("--stages", action="store_true", help="also time every stage")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="adaptive expert top-p (0: off): the router keeps the shortest prefix "
+                         "of each token's top-k whose routing mass reaches this share")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy five times (the known-size kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": 5}))
+        return
+
+    if args.workload == "requant":
+        return bench_requant(args)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU sharding is a design "
+                                   "only (expert-parallel by router group), --gpus must be 1"}))
+        sys.exit(2)
+
+    res = run_workload(args, args.workload, args.steps, args.warmup, not args.no_cpu_baseline,
+                       replays=args.replays, ab_lib=args.ab)
+    if args.workload == "c2" and not args.no_prefill and not args.top_p:
+        # the prefill workload on the same box, GPU only: the grouped GEMM on
+        # the matrix cores
+        pf_args = argparse.Namespace(**{**vars(args), "stages": False})
+        pf = run_workload(pf_args, "c3", 20, 5, False, replays=args.replays)
+        res["prefill"] = {
+            "workload": pf["config"]["workload"],
+            "steps": pf["steps"],
+            "ms_per_step": pf["ms_per_step"],
+            "tokens_per_s": pf["value"],
+            "step_us": pf.get("step_us"),
+            "gate_up_tflops": pf["roofline"]["achieved"],
+            "gate_up_mfma_frac": pf["roofline"]["frac"],
+            "gate_up_us": pf["roofline"]["avg_launch_us"],
+            "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+        }
     print(json.dumps(res), flush=True)
 
 

@@ -64,33 +64,39 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build(); "
                                "there is no fallback implementation")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
-                                 ctypes.c_size_t)
-        D = ctypes.POINTER(MoeLayerDesc)
-        S = ctypes.POINTER(MoeExpertSet)
-        W = ctypes.POINTER(MoeLayerWeights)
-        O = ctypes.POINTER(MoeLaunchOpts)
-        sig = {
-            "moe_workspace_bytes": ([D, i32], sz),
-            "moe_route": ([D, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
-            "moe_bucket": ([i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
-            "moe_expert_ffn": ([D, S, i32, i32, vp, vp, i32, i32, vp, vp, sz, vp], i32),
-            "moe_layer_forward": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp], i32),
-            "moe_layer_forward_ex": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp, O], i32),
-            "moe_layer_forward_noalloc": ([D, W, vp, i32, vp, vp, vp, vp], i32),
-            "moe_rmsnorm": ([vp, i32, i32, f32, vp, vp], i32),
-            "moe_stack_forward": ([D, W, i32, vp, i32, vp, vp, sz, vp], i32),
-            "moe_dequant_rows": ([i32, vp, vp, i32, i32, i32, vp, vp, vp], i32),
-            "moe_status_str": ([i32], ctypes.c_char_p),
-            "moe_requant_fp8_int4": ([vp, vp, i32, i32, i32, vp, vp, vp], i32),
-        }
-        for name, (args, res) in sig.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str):
+    """A libmoe.so at `path` with the C ABI's signatures declared (the in-tree
+    build is lib(); a benchmark A/B loads another build this way)."""
+    L = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    D = ctypes.POINTER(MoeLayerDesc)
+    S = ctypes.POINTER(MoeExpertSet)
+    W = ctypes.POINTER(MoeLayerWeights)
+    O = ctypes.POINTER(MoeLaunchOpts)
+    sig = {
+        "moe_workspace_bytes": ([D, i32], sz),
+        "moe_route": ([D, vp, vp, vp, i32, vp, vp, vp, sz, vp], i32),
+        "moe_bucket": ([i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_expert_ffn": ([D, S, i32, i32, vp, vp, i32, i32, vp, vp, sz, vp], i32),
+        "moe_layer_forward": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp], i32),
+        "moe_layer_forward_ex": ([D, W, vp, i32, vp, vp, vp, vp, sz, vp, O], i32),
+        "moe_layer_forward_noalloc": ([D, W, vp, i32, vp, vp, vp, vp], i32),
+        "moe_rmsnorm": ([vp, i32, i32, f32, vp, vp], i32),
+        "moe_stack_forward": ([D, W, i32, vp, i32, vp, vp, sz, vp], i32),
+        "moe_dequant_rows": ([i32, vp, vp, i32, i32, i32, vp, vp, vp], i32),
+        "moe_status_str": ([i32], ctypes.c_char_p),
+        "moe_requant_fp8_int4": ([vp, vp, i32, i32, i32, vp, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
 
 
 def status_str(status: int) -> str:
