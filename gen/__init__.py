@@ -163,7 +163,8 @@ _host = None
 def host_lib():
     global _host
     if _host is None:
-        path = os.path.join(HERE, "libmoe_gen.so")
+        # MOE_GEN_LIB lets the sanitizer test load an instrumented build
+        path = os.environ.get("MOE_GEN_LIB") or os.path.join(HERE, "libmoe_gen.so")
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
         lib = ctypes.CDLL(path)

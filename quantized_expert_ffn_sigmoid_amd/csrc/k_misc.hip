@@ -10,12 +10,15 @@ namespace moe {
 // ("colibri" README, "What's implemented": routed_scaling_factor-weighted
 // combine with a shared expert; the scaling is already inside w).
 // With a residual: y_copy (optional) = the MoE output, out = residual + it.
+// residual and out may be the same buffer (a stack adds each layer into the
+// running hidden state in place): each thread reads its four residual values
+// before it writes the same four outputs, and neither pointer is restrict.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
                                                  const int32_t* __restrict__ topk_idx,
                                                  const float* __restrict__ topk_w,
                                                  const float* __restrict__ S, int32_t K,
-                                                 int32_t H, const float* __restrict__ residual,
-                                                 float* __restrict__ out,
+                                                 int32_t H, const float* residual,
+                                                 float* out,
                                                  float* __restrict__ y_copy) {
   const int64_t t = blockIdx.y;
   const int o = (blockIdx.x * 256 + threadIdx.x) * 4;
