@@ -119,6 +119,80 @@ __device__ __forceinline__ void gg_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// The wave's weight rows (N-subtile ns, lane row ln): down, 64 consecutive
+// output rows; gate/up, 32 gate rows (ns 0, 1) and the up rows paired with
+// them (ns 2, 3), so that SwiGLU is applied in registers.
+template <bool DOWN>
+__device__ __forceinline__ void gg_weight_rows(const GgTile& t, int rows, int wave, int ln,
+                                               int64_t (&wrow)[4]) {
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    if (DOWN) {
+      wrow[ns] = (int64_t)t.nt * 256 + wave * GG_NW + ns * 16 + ln;
+    } else {
+      const int c = t.nt * 128 + wave * 32 + (ns & 1) * 16 + ln;
+      wrow[ns] = ns < 2 ? c : rows + c;
+    }
+  }
+}
+
+// Per tile row (thread r < 64): the output row index and, for int4, the
+// activation row sum that removes the operand offset.
+template <bool I4, bool DOWN>
+__device__ __forceinline__ void gg_row_meta(const GgArgs& a, const GgTile& t, int& row, float& rs) {
+  row = 0;
+  rs = 0.f;
+  if (threadIdx.x < GG_BM) {
+    const int r = min((int)threadIdx.x, t.n - 1);
+    const int pos = t.p0 + r;
+    if (DOWN) {
+      row = t.shared ? pos : a.entries[pos];
+      if (I4) rs = t.shared ? a.rs_hs[pos] : a.rs_h[pos];
+    } else {
+      row = pos;
+      if (I4) rs = a.rs_x[t.shared ? pos : a.entries[pos] / a.top_k];
+    }
+  }
+}
+
+// Epilogue: lane holds rows m = 16 ms + 4 kg + j of column (weight row) ln
+// of each N-subtile.  gate/up of int4 experts writes h in the order their
+// down projection reads it (0,2,4,6,1,3,5,7 within groups of 8).
+template <bool I4, bool DOWN, int MS>
+__device__ __forceinline__ void gg_epilogue(const GgArgs& a, const GgTile& t, int rows, int kg,
+                                            const f32x4 (&acc)[MS][4], const int64_t (&wrow)[4],
+                                            const float (&sc)[4], const int32_t* s_row,
+                                            const float* s_rs) {
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = ms * 16 + kg * 4 + j;
+      if (m >= t.n) continue;
+      const float off = I4 ? GG_OFF * s_rs[m] : 0.f;
+      const int64_t orow = s_row[m];
+      if constexpr (DOWN) {
+        float* yrow = (t.shared ? a.y_s : a.y) + orow * a.H;
+#pragma unroll
+        for (int ns = 0; ns < 4; ++ns) yrow[wrow[ns]] = sc[ns] * (acc[ms][ns][j] - off);
+      } else {
+        uint16_t* hrow = (t.shared ? a.h_s : a.h) + orow * rows;
+        float* prow = t.shared ? a.hp_s : a.hp;
+#pragma unroll
+        for (int ns = 0; ns < 2; ++ns) {
+          const float g = sc[ns] * (acc[ms][ns][j] - off);
+          const float u = sc[ns + 2] * (acc[ms][ns + 2][j] - off);
+          const int64_t c = wrow[ns];
+          const int64_t pc = I4 ? (c & ~7) | ((c & 1) ? 4 + ((c & 7) >> 1) : (c & 7) >> 1) : c;
+          const float hv = g / (1.0f + expf(-g)) * u;
+          hrow[pc] = f32_to_bf16_bits(hv);
+          if (prow) prow[orow * rows + c] = hv;
+        }
+      }
+    }
+  }
+}
+
 // One tile.  WDT: weight format (MOE_I4 or MOE_BF16); DOWN: down projection
 // (else gate/up + SwiGLU); GRP: K steps per weight load (int4: 1 or 2; each
 // lane then reads 16 * GRP contiguous bytes of each of its rows); NW: K steps
@@ -157,17 +231,8 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
                                                         : ws.gus + (int64_t)t.e * ws.gus_stride);
   const int64_t rowb = I4 ? K / 2 : (int64_t)K * 2;
 
-  // the wave's weight rows: N-subtile ns, lane row ln
   int64_t wrow[4];
-#pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    if (DOWN) {
-      wrow[ns] = (int64_t)t.nt * 256 + wave * GG_NW + ns * 16 + ln;
-    } else {
-      const int c = t.nt * 128 + wave * 32 + (ns & 1) * 16 + ln;
-      wrow[ns] = ns < 2 ? c : rows + c;
-    }
-  }
+  gg_weight_rows<DOWN>(t, rows, wave, ln, wrow);
   const uint8_t* wp[4];
 #pragma unroll
   for (int ns = 0; ns < 4; ++ns) wp[ns] = W + wrow[ns] * rowb;
@@ -181,19 +246,9 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   for (int ns = 0; ns < 4; ++ns) sc[ns] = I4 ? S[wrow[ns]] : 1.0f;
   int32_t* s_row = reinterpret_cast<int32_t*>(lds + 2 * GG_XSTAGE);
   float* s_rs = reinterpret_cast<float*>(s_row + GG_BM);
-  int meta_row = 0;
-  float meta_rs = 0.f;
-  if (threadIdx.x < GG_BM) {
-    const int r = min((int)threadIdx.x, t.n - 1);
-    const int pos = t.p0 + r;
-    if (DOWN) {
-      meta_row = t.shared ? pos : a.entries[pos];
-      if (I4) meta_rs = t.shared ? a.rs_hs[pos] : a.rs_h[pos];
-    } else {
-      meta_row = pos;
-      if (I4) meta_rs = a.rs_x[t.shared ? pos : a.entries[pos] / a.top_k];
-    }
-  }
+  int meta_row;
+  float meta_rs;
+  gg_row_meta<I4, DOWN>(a, t, meta_row, meta_rs);
 
   // Activation loads: thread (rb = tid / 16, p = tid % 16) moves stored
   // position p of tile rows rb + 16 i (i < 4), which holds logical piece
@@ -316,37 +371,152 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
     }
   }
 
-  // epilogue: lane holds rows m = 16 ms + 4 kg + j of column (weight row) ln
-  // of each N-subtile.  gate/up of int4 experts writes h in the order their
-  // down projection reads it (0,2,4,6,1,3,5,7 within groups of 8).
+  gg_epilogue<I4, DOWN, MS>(a, t, rows, kg, acc, wrow, sc, s_row, s_rs);
+}
+
+// Waits until at most N vector memory loads of this wave are outstanding.
+// The asm form keeps memory accesses from moving across the wait; the
+// builtin repeats it in a form the compiler's own wait insertion sees.
+template <int N>
+__device__ __forceinline__ void gg_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  // gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their
+  // maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void* gg_lds_ptr;
+
+// Activation stages of the direct-load tile: D + 1 of them, each MS * 16 rows
+// of 256 bytes laid out as in GG_XSTAGE.
+constexpr int GG_LDS_D = 3;
+constexpr int GG_LDS_DIRECT = (GG_LDS_D + 1) * GG_XSTAGE;
+
+// One int4 tile whose activations go from memory straight into the LDS
+// stages (global_load_lds), D steps ahead of the step that reads them, and
+// whose weights go to registers D steps ahead too, one K step (16 bytes of
+// each of the lane's four rows) per load.  Against the register-staged tile
+// (gg_run) this frees the activation registers and, with both streams the
+// same distance ahead, a wait for one step's activations never holds back on
+// a later step's weights: loads complete in issue order, and every load
+// issued before a step's activations is needed by that step or an earlier
+// one.  At the start of step kt the loads of steps kt + 1 .. kt + D - 1 (MS
+// activation loads and 4 weight loads each) may still be in flight; the
+// barrier after the wait publishes every wave's activation stage and frees
+// the stage of step kt - 1, which the block refills with step kt + D.
+// Steps past the end reload the last one (every wave issues the same loads,
+// so the counts hold to the end).  K order within a step is that of gg_run
+// with GRP = 1.
+template <bool DOWN, int MS, int D>
+__device__ __forceinline__ void gg_run_lds(const GgArgs& a, const GgTile& t, uint8_t* lds) {
+  constexpr int S = D + 1;
+  static_assert(S * GG_XSTAGE <= GG_LDS_DIRECT, "stages fit the block's LDS");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15, kg = lane >> 4;
+  const ExpertSetDev& ws = t.shared ? a.ws : a.w;
+  const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
+  const int rows = DOWN ? a.H : (t.shared ? a.Is : a.I);
+  const uint8_t* W = DOWN ? ws.dn + (int64_t)t.e * ws.dn_stride : ws.gu + (int64_t)t.e * ws.gu_stride;
+  const float* Sc = reinterpret_cast<const float*>(DOWN ? ws.dns + (int64_t)t.e * ws.dns_stride
+                                                         : ws.gus + (int64_t)t.e * ws.gus_stride);
+  const int64_t rowb = K / 2;
+  int64_t wrow[4];
+  gg_weight_rows<DOWN>(t, rows, wave, ln, wrow);
+  const uint8_t* wp[4];
+  float sc[4];
 #pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
+  for (int ns = 0; ns < 4; ++ns) {
+    wp[ns] = W + wrow[ns] * rowb + kg * 16;
+    sc[ns] = Sc[wrow[ns]];
+  }
+  int32_t* s_row = reinterpret_cast<int32_t*>(lds + GG_LDS_DIRECT);
+  float* s_rs = reinterpret_cast<float*>(s_row + GG_BM);
+  int meta_row;
+  float meta_rs;
+  gg_row_meta<true, DOWN>(a, t, meta_row, meta_rs);
+
+  // Activation loads: one instruction of wave w fills 1 KB of a stage, rows
+  // 4w + 16i .. 4w + 16i + 3; lane l takes row 4w + 16i + (l >> 4), stored
+  // position l & 15, which holds logical piece (l & 15) ^ (row % 16).
+  const int xp = lane & 15, xr = 4 * wave + (lane >> 4);
+  const int xc = xp ^ xr;
+  const uint8_t* xsrc[MS];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = ms * 16 + kg * 4 + j;
-      if (m >= t.n) continue;
-      const float off = I4 ? GG_OFF * s_rs[m] : 0.f;
-      const int64_t orow = s_row[m];
-      if constexpr (DOWN) {
-        float* yrow = (t.shared ? a.y_s : a.y) + orow * a.H;
+  for (int i = 0; i < MS; ++i) {
+    const int rr = min(xr + 16 * i, t.n - 1);
+    const uint16_t* row;
+    if (DOWN) {
+      row = (t.shared ? a.h_s : a.h) + (int64_t)(t.p0 + rr) * K;
+    } else {
+      const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
+      row = a.x_p + (int64_t)tok * K;
+    }
+    xsrc[i] = reinterpret_cast<const uint8_t*>(row) + xc * 16;
+  }
+  const int nk = K / GG_BK;
+  auto issue_x = [&](int kt, int stage) {
 #pragma unroll
-        for (int ns = 0; ns < 4; ++ns) yrow[wrow[ns]] = sc[ns] * (acc[ms][ns][j] - off);
-      } else {
-        uint16_t* hrow = (t.shared ? a.h_s : a.h) + orow * rows;
-        float* prow = t.shared ? a.hp_s : a.hp;
+    for (int i = 0; i < MS; ++i)
+      __builtin_amdgcn_global_load_lds(xsrc[i] + (int64_t)kt * (GG_BK * 2),
+                                       (gg_lds_ptr)(lds + stage * GG_XSTAGE + (4 * wave + 16 * i) * (GG_BK * 2)),
+                                       16, 0, 0);
+  };
+  u32x4g wbuf[S][4];
+  auto issue_w = [&](int kt, u32x4g (&v)[4]) {
 #pragma unroll
-        for (int ns = 0; ns < 2; ++ns) {
-          const float g = sc[ns] * (acc[ms][ns][j] - off);
-          const float u = sc[ns + 2] * (acc[ms][ns + 2][j] - off);
-          const int64_t c = wrow[ns];
-          const int64_t pc = I4 ? (c & ~7) | ((c & 1) ? 4 + ((c & 7) >> 1) : (c & 7) >> 1) : c;
-          const float hv = g / (1.0f + expf(-g)) * u;
-          hrow[pc] = f32_to_bf16_bits(hv);
-          if (prow) prow[orow * rows + c] = hv;
+    for (int ns = 0; ns < 4; ++ns) v[ns] = *reinterpret_cast<const u32x4g*>(wp[ns] + (int64_t)kt * 64);
+  };
+
+  f32x4 acc[MS][4];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    issue_x(min(j, nk - 1), j);
+    issue_w(min(j, nk - 1), wbuf[j]);
+  }
+  if (threadIdx.x < GG_BM) {
+    s_row[threadIdx.x] = meta_row;
+    s_rs[threadIdx.x] = meta_rs;
+  }
+  // unrolled by S so that stages and register sets have fixed names
+  for (int kt0 = 0; kt0 < nk; kt0 += S) {
+#pragma unroll
+    for (int st = 0; st < S; ++st) {
+      const int kt = kt0 + st;
+      gg_wait_vm<(D - 1) * (MS + 4)>();
+      gg_barrier();
+      issue_x(min(kt + D, nk - 1), (st + D) % S);
+      issue_w(min(kt + D, nk - 1), wbuf[(st + D) % S]);
+      if (kt < nk) {
+        const uint8_t* xs = lds + st * GG_XSTAGE;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          bf16x8 av[MS];
+#pragma unroll
+          for (int ms = 0; ms < MS; ++ms)
+            av[ms] = as_bf16x8(*reinterpret_cast<const u32x4g*>(
+                xs + (16 * ms + ln) * (GG_BK * 2) + 16 * ((kg * 4 + d) ^ ln)));
+#pragma unroll
+          for (int ns = 0; ns < 4; ++ns) {
+            const u32x4g wq = wbuf[st][ns];
+            const uint32_t w = d == 0 ? wq.x : d == 1 ? wq.y : d == 2 ? wq.z : wq.w;
+            const bf16x8 bv = as_bf16x8(i4_to_bf16(w));
+#pragma unroll
+            for (int ms = 0; ms < MS; ++ms)
+              acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[ms], bv, acc[ms][ns], 0, 0, 0);
+          }
         }
       }
     }
   }
+  // the trailing reloads land before the block's LDS is released
+  gg_wait_vm<0>();
+  gg_epilogue<true, DOWN, MS>(a, t, rows, kg, acc, wrow, sc, s_row, s_rs);
 }
 
 // The M-subtile count of a tile follows its valid rows.
@@ -358,14 +528,24 @@ __device__ __forceinline__ void gg_run_m(const GgArgs& a, const GgTile& t, uint8
 }
 
 // int4 tiles run two waves per SIMD (two blocks per CU), so that one wave's
-// int4 unpacking and waits overlap the other's matrix instructions: weights
-// by pairs of K steps, two pairs in flight (64 registers), two activation
-// sets.  bf16 tiles (64 weight registers per step) run one wave per SIMD
-// with two weight steps and four activation sets in flight.
+// int4 unpacking and waits overlap the other's matrix instructions.  Tiles
+// of more than 16 rows take the direct-load pipeline, 3 steps ahead; tiles of
+// at most 16 rows, whose steps are short and whose time is the weight stream,
+// take the register-staged one with weights by pairs of K steps, two pairs
+// in flight (64 registers), and two activation sets -- on the grouped GEMM
+// of 16384 (token, expert) rows of the 6144 x 2048 layer this split was the
+// faster of the two pipelines for each tile size.  bf16 tiles (64 weight
+// registers per step) run one wave per SIMD with two weight steps and four
+// activation sets in flight.
 template <bool DOWN>
 __device__ __forceinline__ void gg_dispatch_i4(const GgArgs& a, const GgTile& t, uint8_t* lds) {
   const int K = DOWN ? (t.shared ? a.Is : a.I) : a.H;
   const int nk = K / GG_BK;
+  if (nk % 4 == 0 && t.n > 16) {
+    if (t.n > 32) gg_run_lds<DOWN, 4, GG_LDS_D>(a, t, lds);
+    else gg_run_lds<DOWN, 2, GG_LDS_D>(a, t, lds);
+    return;
+  }
   if (nk % 2 == 0) {
     if (nk % 4 == 0) gg_run_m<MOE_I4, DOWN, 2, 4, 2, false>(a, t, lds);
     else gg_run_m<MOE_I4, DOWN, 2, 4, 2, true>(a, t, lds);
@@ -383,12 +563,15 @@ __device__ __forceinline__ void gg_dispatch_bf16(const GgArgs& a, const GgTile& 
 }
 
 constexpr int GG_LDS = 2 * GG_XSTAGE + 2 * GG_BM * 4;
+constexpr int GG_LDS_I4 = (GG_LDS_DIRECT > 2 * GG_XSTAGE ? GG_LDS_DIRECT : 2 * GG_XSTAGE) +
+                          2 * GG_BM * 4;
 
 // One launch covers tiles of one weight format: the routed tiles (when
-// max_tiles > 0) and the shared expert's (when has_shared).
+// max_tiles > 0) and the shared expert's (when has_shared).  Two int4 blocks
+// (64.5 KB of LDS each) share a CU.
 template <bool DOWN>
 __global__ __launch_bounds__(GG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ggemm_i4(GgArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_LDS];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[GG_LDS_I4];
   GgTile t;
   if (!gg_tile(a, t)) return;
   gg_dispatch_i4<DOWN>(a, t, lds);
