@@ -52,7 +52,13 @@ __global__ __launch_bounds__(256) void k_logits_gemv(const float* __restrict__ W
   logits_row_block(W, x, act_bf16, T, H, E, z, sr, blockIdx.x, &red[0][0]);
 }
 
-// Prefill shape: 64 tokens x 64 experts per block, fp64 FMA on LDS tiles.
+// Prefill shape: 64 tokens x 64 experts per block on the fp64 matrix cores
+// (v_mfma_f64_16x16x4_f64): the fp32 operands are widened to fp64 when staged
+// in LDS, so every product is exact and each output is summed in fp64, four
+// K values per instruction in K order.  Each of the 4 waves owns a 32 x 32
+// quadrant (2 x 2 instruction tiles).  Operand layout of the instruction:
+// lane l supplies A[l % 16][l / 16] (token row, K) and B[l / 16][l % 16]
+// (K, expert column) and receives D[l / 16 + 4 r][l % 16], r = 0..3.
 // With split K (gridDim.z chunks of kc), chunk c writes its partial sums to
 // z + c * T * E and k_logits_reduce adds the chunks in order.
 constexpr int LG_BT = 64, LG_BE = 64, LG_BK = 16;
@@ -60,65 +66,72 @@ __global__ __launch_bounds__(256) void k_logits_gemm(const float* __restrict__ W
                                                      const void* __restrict__ x, int act_bf16,
                                                      int32_t T, int32_t H, int32_t E, int32_t kc,
                                                      double* __restrict__ z) {
-  // operands widened to fp64 once, when staged (each is used by 4 threads'
-  // 4 x 4 tiles)
+  // operands widened to fp64 once, when staged (each is read by the two
+  // waves whose quadrants share its rows or columns)
   __shared__ double sx[LG_BK][LG_BT + 2];
   __shared__ double sw[LG_BK][LG_BE + 2];
   const int t0 = blockIdx.x * LG_BT, e0 = blockIdx.y * LG_BE;
   const int kbeg = blockIdx.z * kc, kend = kbeg + kc;
   z += (int64_t)blockIdx.z * T * E;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4];
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int qr = (wave >> 1) * 32, qc = (wave & 1) * 32;   // the wave's quadrant
+  const int li = lane & 15, lk = lane >> 4;
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
   // each thread stages 4 consecutive k of one row of x and of W; the next
   // step's values are loaded into registers while the current step computes
-  const int lr = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;
+  const int lr = threadIdx.x >> 2, sk = (threadIdx.x & 3) * 4;
   const int t = t0 + lr, e = e0 + lr;
   float4 v = make_float4(0.f, 0.f, 0.f, 0.f), w = make_float4(0.f, 0.f, 0.f, 0.f);
   auto load = [&](int k0) {
-    if (t < T) v = load_x4(x, act_bf16, (int64_t)t * H + k0 + lk);
-    if (e < E) w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + k0 + lk);
+    if (t < T) v = load_x4(x, act_bf16, (int64_t)t * H + k0 + sk);
+    if (e < E) w = *reinterpret_cast<const float4*>(W + (int64_t)e * H + k0 + sk);
   };
   // workgroup barrier after this wave's LDS accesses, without the release
   // fence of __syncthreads (which would also wait for the loads in flight)
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
   if (kbeg < kend) load(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += LG_BK) {
-    sx[lk + 0][lr] = (double)v.x;
-    sx[lk + 1][lr] = (double)v.y;
-    sx[lk + 2][lr] = (double)v.z;
-    sx[lk + 3][lr] = (double)v.w;
-    sw[lk + 0][lr] = (double)w.x;
-    sw[lk + 1][lr] = (double)w.y;
-    sw[lk + 2][lr] = (double)w.z;
-    sw[lk + 3][lr] = (double)w.w;
+    sx[sk + 0][lr] = (double)v.x;
+    sx[sk + 1][lr] = (double)v.y;
+    sx[sk + 2][lr] = (double)v.z;
+    sx[sk + 3][lr] = (double)v.w;
+    sw[sk + 0][lr] = (double)w.x;
+    sw[sk + 1][lr] = (double)w.y;
+    sw[sk + 2][lr] = (double)w.z;
+    sw[sk + 3][lr] = (double)w.w;
     lds_barrier();
     if (k0 + LG_BK < kend) load(k0 + LG_BK);
 #pragma unroll
-    for (int k = 0; k < LG_BK; ++k) {
-      double a[4], b[4];
+    for (int k = 0; k < LG_BK; k += 4) {
+      double a[2], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sx[k][ty * 4 + i];
+      for (int i = 0; i < 2; ++i) a[i] = sx[k + lk][qr + 16 * i + li];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = sw[k][tx * 4 + j];
+      for (int j = 0; j < 2; ++j) b[j] = sw[k + lk][qc + 16 * j + li];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     lds_barrier();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) z[(int64_t)t * E + e] = acc[i][j];
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + qr + 16 * i + lk + 4 * r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int e = e0 + qc + 16 * j + li;
+        if (e < E) z[(int64_t)t * E + e] = acc[i][j][r];
+      }
     }
   }
 }
