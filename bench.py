@@ -461,15 +461,18 @@ def run_workload(args, wl, K, W, with_cpu, replays=5, ab_lib=None):
         stage_ms[s_id] = [hip.elapsed_ms(evs[i][k][0], evs[i][k][1]) for i in range(K)]
     # The event bracket holds the kernel plus what the two event nodes add
     # around running work.  That is measured on whole steps: a bracket around
-    # each step of a replay of its own, less the event-free time per step.
-    # (An empty event pair, also printed, takes longer than the nodes add
-    # around a kernel.)  Medians over the steps, as a few brackets now and
-    # then take several times their usual time.
+    # each step of a replay of its own, less the event-free time per step
+    # (the median over the event-timed replays of the step graph; the host
+    # clock's step time when there are none).  An empty event pair, also
+    # printed, takes longer than the nodes add around a kernel.  Medians over
+    # the steps, as a few brackets now and then take several times their
+    # usual time.
     bracket_ms = float(np.median(stage_ms[capi.MOE_STAGE_GATE_UP]))
     pair_ms = float(np.median([hip.elapsed_ms(a, b) for a, b in evp]))
     whole = [hip.elapsed_ms(a, b) for a, b in evw]
     whole_ms = float(np.median(whole))
-    over_ms = whole_ms - ms_step
+    free_ms = float(np.median(rep_ms)) if rep_ms else ms_step
+    over_ms = whole_ms - free_ms
     gu_ms = bracket_ms - over_ms if 0.0 < over_ms < 0.5 * bracket_ms else bracket_ms
     gu_bytes = float(np.mean([gate_up_bytes(cfg, dtype, n, T) for n in n_active[:K]]))
     lay_bytes = float(np.mean([layer_bytes(cfg, dtype, n, T) for n in n_active[:K]]))

@@ -162,9 +162,12 @@ moe_status moe_expert_ffn(const moe_layer_desc* d, const moe_expert_set* set, in
                           int32_t expert, const void* x, const int32_t* rows, int32_t n_rows,
                           int32_t row_div, float* y, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole routed layer: route, bucket, apply each active expert once to all
- * of its tokens, and combine: out[t] = sum_j topk_w[t][j] * FFN_{e_tj}(x_t)
- * (j ascending) + shared(x_t).  x: [n_tokens][H] act_dtype; out: [n_tokens][H]
+/* The whole routed layer ("colibri" README, "The idea" -- a shared expert
+ * beside the routed ones -- and "What's implemented" -- the sigmoid router,
+ * batch-union grouping and the routed_scaling-weighted combine; "iliria"
+ * README, "What's implemented": the SwiGLU expert over one activation): route,
+ * bucket, apply each active expert once to all of its tokens, and combine:
+ * out[t] = sum_j topk_w[t][j] * FFN_{e_tj}(x_t) (j ascending) + shared(x_t).  x: [n_tokens][H] act_dtype; out: [n_tokens][H]
  * fp32.  topk_idx_out / topk_w_out ([n_tokens][k]) are optional copies of the
  * routing.  Workspace: moe_workspace_bytes(d, n_tokens).
  * Two expert paths: up to 16 tokens, dequant-on-use GEMV kernels; more
@@ -183,9 +186,14 @@ moe_status moe_layer_forward(const moe_layer_desc* d, const moe_layer_weights* w
  * events[2s+1] right after them.  While the stream is being captured into a
  * graph the records are external event nodes, so each replay times the stage. */
 /* Decode batches (<= 16 tokens) whose shared expert streams through the
- * GEMV ring (sigmoid router, <= 256 experts) run the shared expert inside the
- * ROUTE stage: the logits launch also holds its gate/up, the selection launch
- * its down projection; GATE_UP and DOWN then hold the routed experts only. */
+ * GEMV ring (sigmoid router, <= 256 experts) run the shared expert's gate/up
+ * inside the ROUTE stage (the logits launch holds it).  With 2..16 tokens the
+ * selection launch, also in ROUTE, holds its down projection; GATE_UP and
+ * DOWN then hold the routed experts only.  With one token (int4, int8 or
+ * bf16 experts on the ring): ROUTE holds the logits and the shared gate/up;
+ * GATE_UP holds the selection and grouping (run inside every routed gate/up
+ * block) and the routed gate/up; DOWN holds the routed and shared down
+ * projections and the combine in one launch; BUCKET and COMBINE are empty. */
 enum {
   MOE_STAGE_ROUTE = 0,     /* router logits + selection (+ grouping, for <= 16 tokens) */
   MOE_STAGE_BUCKET = 1,    /* batch-union grouping (empty when fused into ROUTE)      */
@@ -208,7 +216,14 @@ moe_status moe_layer_forward_ex(const moe_layer_desc* d, const moe_layer_weights
                                 int32_t* topk_idx_out, float* topk_w_out, void* ws,
                                 size_t ws_bytes, void* stream, const moe_launch_opts* opts);
 
-/* RMSNorm with unit gain, out = x / sqrt(mean(x^2) + eps), computed in fp64
+/* Stack glue.  The pages describe one MoE layer; the stacked workloads (a
+ * 24-layer Granite-shaped stack and 8 stacked GLM-shaped layers) need the
+ * residual and the pre-norm between layers, which the pages leave to the
+ * surrounding model.  moe_rmsnorm and moe_stack_forward provide that glue
+ * with the plainest reading: RMSNorm with unit gain (eps from the descriptor,
+ * 1e-6 in those stacks), residual added in fp32.
+ *
+ * RMSNorm with unit gain, out = x / sqrt(mean(x^2) + eps), computed in fp64
  * and rounded to fp32.  x, out: [n_tokens][hidden] fp32 (may alias). */
 moe_status moe_rmsnorm(const float* x, int32_t n_tokens, int32_t hidden, float eps, float* out,
                        void* stream);
