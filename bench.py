@@ -152,9 +152,9 @@ def _ring(dtype, K):
     """Whether the expert GEMV streams rows of length K of this format through
     its LDS ring (64 lanes on a row, a compiled slice length)."""
     if dtype == gen.BF16:
-        return K % 512 == 0 and K // 64 in (8, 16, 32, 64, 96)
+        return K % 512 == 0 and K // 64 in (8, 16, 32, 64, 96, 112, 128)
     if dtype in (gen.I4, gen.I8, gen.I2):
-        return K % 2048 == 0 and K // 64 in (32, 64, 96)
+        return K % 2048 == 0 and K // 64 in (32, 64, 96, 128)
     return False
 
 

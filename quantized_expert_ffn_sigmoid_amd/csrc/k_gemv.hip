@@ -15,8 +15,12 @@ static bool geo_for(int32_t K, MatGeo& g) {
   if (lpr & (lpr - 1)) return false;
   if (gran % lpr) return false;
   const int ksl = K / lpr;
-  const bool ok = WDT == MOE_BF16 ? (ksl == 8 || ksl == 16 || ksl == 32 || ksl == 64 || ksl == 96)
-                                  : (ksl == 32 || ksl == 64 || ksl == 96);
+  // (K 6144 -> 96; K 8192 -> 128 for every format; K 7168 -> 112 for bf16
+  // only, as 112 codes per lane are not whole 32-code granules of the
+  // integer formats)
+  const bool ok = WDT == MOE_BF16 ? (ksl == 8 || ksl == 16 || ksl == 32 || ksl == 64 ||
+                                     ksl == 96 || ksl == 112 || ksl == 128)
+                                  : (ksl == 32 || ksl == 64 || ksl == 96 || ksl == 128);
   if (!ok) return false;
   g.lpr = lpr;
   g.rpp = 64 / lpr;

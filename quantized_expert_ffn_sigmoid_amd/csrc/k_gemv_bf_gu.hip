@@ -14,6 +14,8 @@ hipError_t gemv_bf_gu(const GemvArgs& a, int ws_dtype, int ntmax, int act_bf16, 
   if (k == 32) return gemv_go<MOE_BF16, 32, MOE_BF16, 32, false>(a, ntmax, act_bf16, blocks, s);
   if (k == 64) return gemv_go<MOE_BF16, 64, MOE_BF16, 64, false>(a, ntmax, act_bf16, blocks, s);
   if (k == 96) return gemv_go<MOE_BF16, 96, MOE_BF16, 96, false>(a, ntmax, act_bf16, blocks, s);
+  if (k == 128) return gemv_go<MOE_BF16, 128, MOE_BF16, 128, false>(a, ntmax, act_bf16, blocks, s);
+  if (k == 112) return gemv_go<MOE_BF16, 112, MOE_BF16, 112, false>(a, ntmax, act_bf16, blocks, s);
   return hipErrorInvalidValue;
 }
 

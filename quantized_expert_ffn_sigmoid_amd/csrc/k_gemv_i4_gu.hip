@@ -14,7 +14,9 @@ hipError_t gemv_i4_gu(const GemvArgs& a, int ws_dtype, int ntmax, int act_bf16, 
   if (k == 64 && same) return gemv_go<MOE_I4, 64, MOE_I4, 64, false>(a, ntmax, act_bf16, blocks, s);
   if (k == 64 && bf) return gemv_go<MOE_I4, 64, MOE_BF16, 64, false>(a, ntmax, act_bf16, blocks, s);
   if (k == 96 && same) return gemv_go<MOE_I4, 96, MOE_I4, 96, false>(a, ntmax, act_bf16, blocks, s);
+  if (k == 128 && same) return gemv_go<MOE_I4, 128, MOE_I4, 128, false>(a, ntmax, act_bf16, blocks, s);
   if (k == 96 && bf) return gemv_go<MOE_I4, 96, MOE_BF16, 96, false>(a, ntmax, act_bf16, blocks, s);
+  if (k == 128 && bf) return gemv_go<MOE_I4, 128, MOE_BF16, 128, false>(a, ntmax, act_bf16, blocks, s);
   return hipErrorInvalidValue;
 }
 

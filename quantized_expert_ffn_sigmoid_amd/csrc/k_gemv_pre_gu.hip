@@ -13,14 +13,18 @@ hipError_t gemv_pre_gu(const GemvArgs& a, const PreArgs& p, int ws_dtype, int ac
     if (k == 32) return gemv_pre_go<MOE_BF16, 32, false>(a, p, act_bf16, blocks, s);
     if (k == 64) return gemv_pre_go<MOE_BF16, 64, false>(a, p, act_bf16, blocks, s);
     if (k == 96) return gemv_pre_go<MOE_BF16, 96, false>(a, p, act_bf16, blocks, s);
+    if (k == 128) return gemv_pre_go<MOE_BF16, 128, false>(a, p, act_bf16, blocks, s);
+    if (k == 112) return gemv_pre_go<MOE_BF16, 112, false>(a, p, act_bf16, blocks, s);
   } else if (ws_dtype == MOE_I4) {
     if (k == 32) return gemv_pre_go<MOE_I4, 32, false>(a, p, act_bf16, blocks, s);
     if (k == 64) return gemv_pre_go<MOE_I4, 64, false>(a, p, act_bf16, blocks, s);
     if (k == 96) return gemv_pre_go<MOE_I4, 96, false>(a, p, act_bf16, blocks, s);
+    if (k == 128) return gemv_pre_go<MOE_I4, 128, false>(a, p, act_bf16, blocks, s);
   } else if (ws_dtype == MOE_I8) {
     if (k == 32) return gemv_pre_go<MOE_I8, 32, false>(a, p, act_bf16, blocks, s);
     if (k == 64) return gemv_pre_go<MOE_I8, 64, false>(a, p, act_bf16, blocks, s);
     if (k == 96) return gemv_pre_go<MOE_I8, 96, false>(a, p, act_bf16, blocks, s);
+    if (k == 128) return gemv_pre_go<MOE_I8, 128, false>(a, p, act_bf16, blocks, s);
   }
   return hipErrorInvalidValue;
 }
