@@ -483,7 +483,8 @@ def run_workload(args, wl, K, W, with_cpu, replays=5, ab_lib=None):
         flops = gate_up_flops(cfg, T)
         tflops = flops / (gu_ms * 1e-3) / 1e12
         roofline = {
-            "kernel": "moe::k_ggemm gate/up + SwiGLU (grouped GEMM, int4 routed + bf16 shared)",
+            "kernel": ("gate/up stage: moe::k_ggemm int4 routed tiles + the bf16 shared expert"
+                       " (hipBLASLt GEMM + moe::k_swiglu_rows at >= 256 tokens)"),
             "bound": "mfma",
             "achieved": round(tflops, 1),
             "peak": MFMA_BF16_PEAK_TFLOPS,

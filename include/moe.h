@@ -16,10 +16,14 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns all
- *     memory; the library allocates nothing and keeps no global state, so it
- *     is safe to call from several host threads on different streams (the
- *     one exception, moe_layer_forward_noalloc, runs on a workspace of the
- *     library's own, one per GPU).
+ *     memory; the library allocates nothing of its own for the data, so it
+ *     is safe to call from several host threads on different streams.  Two
+ *     exceptions: moe_layer_forward_noalloc runs on a workspace of the
+ *     library's own, one per GPU; and layers with a bf16 shared expert, on
+ *     batches of 256 tokens or more, run that expert's two dense GEMMs
+ *     through hipBLASLt, with a handle per GPU and one algorithm per shape
+ *     that the first such call outside graph capture creates and keeps
+ *     (a call captured before any has runs the grouped-GEMM tiles instead).
  *   - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default
  *     stream) and never synchronise: results are valid once the stream has
  *     reached the enqueued work.  A device-side fault surfaces at the caller's

@@ -51,6 +51,33 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ Y,
   *reinterpret_cast<float4*>(out + t * H + o) = acc;
 }
 
+// SwiGLU over fp32 gate/up rows: h[t][c] = bf16(silu(g) * u) with
+// g = GU[t][c], u = GU[t][Is + c] (the dense shared-expert path's gate/up
+// output, "iliria" README, "What's implemented": SwiGLU over one
+// activation); hp (nullable) receives h before rounding.
+__global__ __launch_bounds__(256) void k_swiglu_rows(const float* __restrict__ GU, int32_t T,
+                                                     int32_t Is, uint16_t* __restrict__ h,
+                                                     float* __restrict__ hp) {
+  const int64_t n = (int64_t)T * Is;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i / Is, c = i - t * Is;
+    const float g = GU[t * 2 * Is + c], u = GU[t * 2 * Is + Is + c];
+    const float hv = g / (1.0f + expf(-g)) * u;
+    h[i] = f32_to_bf16_bits(hv);
+    if (hp) hp[i] = hv;
+  }
+}
+
+hipError_t launch_swiglu_rows(const float* gu, int32_t T, int32_t Is, uint16_t* h, float* hp,
+                              hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int64_t n = (int64_t)T * Is;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_swiglu_rows, dim3((unsigned)blocks), dim3(256), 0, s, gu, T, Is, h, hp);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const float* Y, const int32_t* topk_idx, const float* topk_w,
                           const float* S, int32_t T, int32_t K, int32_t H, const float* residual,
                           float* out, float* y_copy, hipStream_t s) {

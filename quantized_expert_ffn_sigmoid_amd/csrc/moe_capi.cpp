@@ -415,18 +415,31 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     q.rs_h = rs + T;
     q.rs_hs = rs + (int64_t)T * (K + 1);
     const bool any_i4 = d.expert_dtype == MOE_I4 || (has_sh && d.shared_dtype == MOE_I4);
+    // A bf16 shared expert over a large batch is two plain dense GEMMs: they
+    // go to the platform's GEMM library (its gate/up output, fp32 [T][2 Is],
+    // in the Y area, which the routed down projection fills only later).
+    const bool sh_dense = has_sh && d.shared_dtype == MOE_BF16 && T >= kSharedDenseMinTokens &&
+                          (int64_t)K * H >= 2 * (int64_t)Ish &&
+                          shared_gemm_ready(s, T, 2 * Ish, H, H, Ish);
+    GgArgs qr = q;
+    if (sh_dense) qr.has_shared = 0;
     MOE_TRY(launch_make_tiles(offsets, active, n_active, tiles, tiles + mt, tiles + 2 * mt,
                               tiles + 3 * mt, tiles + 4 * mt, tiles + 5 * mt, s));
     record(opts, MOE_STAGE_GATE_UP, 0, s);
-    q.x_p = at<uint16_t>(ws, c.xp);
+    q.x_p = qr.x_p = at<uint16_t>(ws, c.xp);
     if (any_i4) MOE_TRY(launch_rowsum_bf16(q.x, T, H, rs, at<uint16_t>(ws, c.xp), s));
-    MOE_TRY(launch_ggemm(q, false, d.expert_dtype, d.shared_dtype, s));
+    MOE_TRY(launch_ggemm(qr, false, d.expert_dtype, d.shared_dtype, s));
+    if (sh_dense) {
+      MOE_TRY(shared_gemm(T, 2 * Ish, H, w.shared.gate_up, x, Y, s));
+      MOE_TRY(launch_swiglu_rows(Y, T, Ish, q.h_s, q.hp_s, s));
+    }
     record(opts, MOE_STAGE_GATE_UP, 1, s);
     record(opts, MOE_STAGE_DOWN, 0, s);
     if (d.expert_dtype == MOE_I4) MOE_TRY(launch_rowsum_bf16(q.h, T * K, I, rs + T, nullptr, s));
     if (has_sh && d.shared_dtype == MOE_I4)
       MOE_TRY(launch_rowsum_bf16(q.h_s, T, Ish, rs + (int64_t)T * (K + 1), nullptr, s));
-    MOE_TRY(launch_ggemm(q, true, d.expert_dtype, d.shared_dtype, s));
+    MOE_TRY(launch_ggemm(qr, true, d.expert_dtype, d.shared_dtype, s));
+    if (sh_dense) MOE_TRY(shared_gemm(T, H, Ish, w.shared.down, q.h_s, S, s));
     record(opts, MOE_STAGE_DOWN, 1, s);
     record(opts, MOE_STAGE_COMBINE, 0, s);
     MOE_TRY(launch_combine(Y, idx, tw, has_sh ? S : nullptr, T, K, H, residual, out, y_copy, s));

@@ -285,6 +285,17 @@ hipError_t launch_make_tiles(const int32_t* offsets, const int32_t* active, cons
                              int32_t* tile_first, int32_t* tile_cnt, int32_t* n_tiles,
                              hipStream_t s);
 hipError_t launch_ggemm(GgArgs a, bool down, int dtype, int shared_dtype, hipStream_t s);
+// The shared expert's dense GEMMs for prefill batches (shared_blaslt.cpp):
+// D[M][N] (fp32, row-major) = B[M][K] (bf16 rows) x A[N][K]^T (bf16 rows).
+// shared_gemm_ready tells whether both of a layer's shapes (gate/up N1 x K1,
+// down N2 x K2) have a handle and an algorithm on the stream's device
+// (prepared on first use outside graph capture).
+constexpr int kSharedDenseMinTokens = 256;
+bool shared_gemm_ready(hipStream_t s, int M, int N1, int K1, int N2, int K2);
+hipError_t shared_gemm(int M, int N, int K, const void* A, const void* B, float* D, hipStream_t s);
+// h = bf16(silu(GU[:, :Is]) * GU[:, Is:]) over T fp32 rows of 2 Is (k_misc.hip)
+hipError_t launch_swiglu_rows(const float* gu, int32_t T, int32_t Is, uint16_t* h, float* hp,
+                              hipStream_t s);
 hipError_t launch_rowsum_bf16(const uint16_t* rows, int32_t n, int32_t K, float* out,
                               uint16_t* perm, hipStream_t s);
 
