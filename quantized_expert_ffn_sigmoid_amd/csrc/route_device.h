@@ -147,13 +147,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(p32[0], p32[1]);
 }
 
-// Wave-wide maximum of 64-bit keys, in every lane: the high words first, then
-// the low words of the lanes that hold the largest high word.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+// The lanes holding the wave-wide maximum of 64-bit keys (a lane mask): the
+// high words first; only when several lanes share the largest high word
+// (the scores then agree to about 2^-20 of their value, rare) the low words
+// of those lanes decide.
+__device__ __forceinline__ uint64_t wave_max_key_lanes(uint64_t k) {
   const uint32_t hi = (uint32_t)(k >> 32);
   const uint32_t mh = wave_max_u32(hi);
+  const uint64_t b = __ballot(hi == mh);
+  if (__popcll(b) == 1) return b;
   const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)k : 0u);
-  return ((uint64_t)mh << 32) | ml;
+  return __ballot(hi == mh && (uint32_t)k == ml);
 }
 
 // Two largest values (a >= b) merged with a partner's pair.
@@ -304,8 +308,7 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
   int my_idx = 0;
   double my_raw = 0.0;
   for (int j = 0; j < p.K; ++j) {
-    const uint64_t m = wave_max_key(hk[0]);
-    const uint64_t b = __ballot(hk[0] == m);
+    const uint64_t b = wave_max_key_lanes(hk[0]);
     const int owner = (int)__builtin_ctzll(b);
     const int ri = __builtin_amdgcn_readlane(hx[0], owner);
     const double s_win = readlane_d(hs[0], owner);
