@@ -1015,7 +1015,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   if ((int)blockIdx.x < p.blocks) {
     if constexpr (!DOWN) {
       logits_row_block(p.w_router, p.x, p.act_bf16, p.T, p.H, p.E, p.z, p.sr, blockIdx.x,
-                       reinterpret_cast<double*>(&lds.ring[0][0][0]));
+                       reinterpret_cast<double*>(&lds.ring[0][0][0]), p.zsc, p.zbias);
     } else {
       select_bucket_block<4, true>(p.sp, p.zin, p.bias, p.T, p.idx, p.w, p.counts, p.offsets,
                                    p.entries, p.inverse, p.active, p.n_active,

@@ -223,6 +223,7 @@ SelectParams select_params(const moe_layer_desc& d) {
   p.topk_group = p.softmax ? 1 : d.topk_group;
   p.scaling = d.routed_scaling;
   p.top_p = (double)d.top_p;
+  p.zsc = nullptr;
   return p;
 }
 

@@ -99,7 +99,7 @@ int32_t epg_of(int32_t dtype) { return dtype == MOE_BF16 ? 8 : 32; }
 // Workspace carve for n tokens.  Every region is 256-byte aligned.
 struct Carve {
   size_t z, idx, w, counts, offsets, entries, inverse, active, n_active, h, h_sh, Y, S, xn, yl,
-      xs, xs_sh, tiles, rs, xp, slot_tab, pos_e, total;
+      xs, xs_sh, tiles, rs, xp, slot_tab, pos_e, zsc, total;
 };
 
 Carve carve(const moe_layer_desc& d, int64_t T) {
@@ -134,6 +134,7 @@ Carve carve(const moe_layer_desc& d, int64_t T) {
   c.xp = take(sizeof(uint16_t) * (size_t)T * H);
   c.slot_tab = take(sizeof(int32_t) * kSlotRec * (size_t)(T * K < E ? T * K : E));
   c.pos_e = take(sizeof(int32_t) * (size_t)T * K);
+  c.zsc = take(sizeof(double) * 2 * (size_t)(T <= kDecodeTokens ? T : 0) * E);
   c.total = o;
   return c;
 }
@@ -272,8 +273,13 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
   // gate/up shares the routed launch, which this variant does not hold)
   const bool sel_inline = fused_dn && (pre || !has_sh) && gemv_sel_supported(d, T);
   PreArgs sel{};
+  // the selection reads the scores the logits launch formed (sigmoid router
+  // with the logits in the shared expert's launch)
+  double* zsc = (sel_inline && pre && d.router == MOE_ROUTER_SIGMOID_NOAUX_TC)
+                    ? at<double>(ws, c.zsc) : nullptr;
   if (sel_inline) {
     sel.sp = select_params(d);
+    sel.sp.zsc = zsc;
     sel.T = T;
     sel.zin = z;
     sel.bias = w.bias;
@@ -305,6 +311,8 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     p.E = E;
     p.z = z;
     p.sr = sr;
+    p.zsc = zsc;
+    p.zbias = w.bias;
     MOE_TRY(launch_gemv_pre(gs, p, false, d.shared_dtype, act_bf16, s));
     if (fused_dn) {
       // the shared down projection joins the routed ones in the fused launch;

@@ -100,6 +100,10 @@ struct SelectParams {
   int32_t E, K, G, topk_group, softmax;
   float scaling;
   double top_p;   // adaptive expert top-p, active when 0 < top_p < 1
+  // nullable (sigmoid router): [T][E][2] the score s = sigmoid(z) and the
+  // biased score s + bias of every expert, written by the logits launch
+  // (the same fp64 operations the selection would run)
+  const double* zsc;
 };
 
 // Routing work that runs in the leading blocks of a shared-expert GEMV launch
@@ -116,6 +120,8 @@ struct PreArgs {
   int32_t act_bf16, T, H, E;
   double* z;
   SliceReq sr;
+  double* zsc;          // nullable: also write the scores (SelectParams::zsc)
+  const float* zbias;   // the router bias for them (nullable)
   // selection + grouping
   SelectParams sp;
   const double* zin;

@@ -194,7 +194,8 @@ __device__ __forceinline__ void wave_top2(double& a, double& b) { segment_top2(a
 template <int EPL, bool SOFTMAX>
 __device__ __forceinline__ void select_token(const SelectParams& p, const double* __restrict__ zt,
                                              const float* __restrict__ bias, int32_t* idx_out,
-                                             float* w_out, int32_t* idx_lds) {
+                                             float* w_out, int32_t* idx_lds,
+                                             const double* sct = nullptr) {
   const int lane = threadIdx.x & 63;
   const double NEG = -INFINITY;
   double c[EPL], sv[EPL];
@@ -203,11 +204,16 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     const int e = lane * EPL + i;
     const bool ok = e < p.E;
     const int ec = ok ? e : p.E - 1;
-    const double zv = zt[ec];
     if constexpr (SOFTMAX) {
+      const double zv = zt[ec];
       sv[i] = zv;
       c[i] = ok ? zv : NEG;
+    } else if (sct) {
+      // the token's scores, formed by the logits launch
+      sv[i] = sct[2 * ec];
+      c[i] = ok ? sct[2 * ec + 1] : NEG;
     } else {
+      const double zv = zt[ec];
       const double s = 1.0 / (1.0 + exp(-zv));
       sv[i] = s;
       const double bb = bias ? (double)bias[ec] : 0.0;
@@ -586,7 +592,8 @@ __device__ __forceinline__ void logits_row_block(const float* __restrict__ W,
                                                  const void* __restrict__ x, int act_bf16,
                                                  int32_t T, int32_t H, int32_t E,
                                                  double* __restrict__ z, const SliceReq& sr,
-                                                 int e, double* red) {
+                                                 int e, double* red, double* zsc = nullptr,
+                                                 const float* zbias = nullptr) {
   const int tid = threadIdx.x;
   {
     const int ab = act_bf16 ? 2 : 4;
@@ -641,7 +648,16 @@ __device__ __forceinline__ void logits_row_block(const float* __restrict__ W,
       for (int n = 0; n < T; ++n) red[n * 256 + tid] += red[n * 256 + tid + st];
     __syncthreads();
   }
-  if (tid < T) z[(int64_t)tid * E + e] = red[tid * 256];
+  if (tid < T) {
+    const double zv = red[tid * 256];
+    z[(int64_t)tid * E + e] = zv;
+    if (zsc) {
+      // the sigmoid router's scores, as select_token forms them
+      const double s = 1.0 / (1.0 + exp(-zv));
+      zsc[((int64_t)tid * E + e) * 2] = s;
+      zsc[((int64_t)tid * E + e) * 2 + 1] = s + (zbias ? (double)zbias[e] : 0.0);
+    }
+  }
 }
 
 // LDS scratch of select_bucket_block.
@@ -667,7 +683,8 @@ __device__ __forceinline__ void select_bucket_block(
                               topk_w + (int64_t)t * p.K, L.idx + t * p.K);
     else
       select_token<EPL, false>(p, z + (int64_t)t * p.E, bias, topk_idx + (int64_t)t * p.K,
-                               topk_w + (int64_t)t * p.K, L.idx + t * p.K);
+                               topk_w + (int64_t)t * p.K, L.idx + t * p.K,
+                               p.zsc ? p.zsc + (int64_t)t * p.E * 2 : nullptr);
   }
   __syncthreads();
   bucket_small(T, p.K, p.E, L.idx, counts, offsets, entries, inverse, active, n_active, L.b, tb);
