@@ -582,6 +582,11 @@ def ab_compare(hip, capi, lib_b, graph_a, sh, out, capture_steps, K, pairs):
     lib_a = capi.lib()
     capi._lib = capi.load_library(lib_b)
     try:
+        # one eager pass first, as the in-tree library had before its capture:
+        # set-up that a library does only outside capture (a GEMM library handle
+        # and its plans) is then in place for B's graph too
+        capture_steps()
+        torch.cuda.synchronize()
         graph_b = hip.capture(sh, capture_steps)
     finally:
         capi._lib = lib_a
