@@ -71,9 +71,9 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t b, bool hi_word) {
 }
 
 __device__ __forceinline__ u32x4u i4_to_bf16(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;
-  const uint32_t lo = u & 0x0F0F0F0Fu;          // codes 0, 2, 4, 6 in bytes 0..3
-  const uint32_t hi = (u >> 4) & 0x0F0F0F0Fu;   // codes 1, 3, 5, 7
+  // mask and offset in one three-input bit operation each
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // codes 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // codes 1, 3, 5, 7
   u32x4u r;
   r.x = fp8x2_to_bf16x2(lo, false);
   r.y = fp8x2_to_bf16x2(lo, true);
