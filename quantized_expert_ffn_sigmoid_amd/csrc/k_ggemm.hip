@@ -595,22 +595,40 @@ __global__ __launch_bounds__(256) void k_make_tiles(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ tile_first,
                                                     int32_t* __restrict__ tile_cnt,
                                                     int32_t* __restrict__ n_tiles) {
+  constexpr int PER = kMaxExperts / 256;   // active experts per thread
   __shared__ int32_t scan[kMaxExperts];
+  __shared__ int32_t part[256];
   const int na = *n_active;
-  for (int s = threadIdx.x; s < na; s += 256) {
-    const int e = active[s];
-    scan[s] = (offsets[e + 1] - offsets[e] + GG_BM - 1) / GG_BM;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int s = 0; s < na; ++s) {
-      const int c = scan[s];
-      scan[s] = run;
-      run += c;
+  const int t = threadIdx.x;
+  // tile counts of the thread's run of PER active experts, and their sum
+  int cnt[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int s = t * PER + i;
+    int c = 0;
+    if (s < na) {
+      const int e = active[s];
+      c = (offsets[e + 1] - offsets[e] + GG_BM - 1) / GG_BM;
     }
-    *n_tiles = run;
+    cnt[i] = c;
+    sum += c;
   }
+  // inclusive scan of the 256 runs' sums (Hillis-Steele in LDS)
+  part[t] = sum;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int add = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int run = part[t] - sum;   // tiles before the thread's run
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    scan[t * PER + i] = run;
+    run += cnt[i];
+  }
+  if (t == 255) *n_tiles = part[255];
   __syncthreads();
   for (int s = threadIdx.x; s < na; s += 256) {
     const int e = active[s];

@@ -375,6 +375,8 @@ constexpr int BK_THREADS = 1024;
 constexpr int BK_WAVES = BK_THREADS / kWave;
 constexpr int BK_KEY_BITS = 10;   // experts < 1024
 constexpr int BK_SMALL = 512;     // slot counts up to this take the direct path
+constexpr int BK_PER = 16;        // slots per thread read ahead by the general path
+constexpr int64_t BK_CHUNK = (int64_t)BK_THREADS * BK_PER;
 
 // LDS scratch of bucket_small (16-byte aligned).
 struct __attribute__((aligned(16))) BucketSmallLds {
@@ -497,9 +499,18 @@ __device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx
     for (int w = 0; w < BK_WAVES; ++w) s_wcnt[w][e] = 0;
   }
   __syncthreads();
-  for (int64_t f = tid; f < F; f += BK_THREADS) {
-    const int e = idx[f];
-    if (e >= 0 && e < E) atomicAdd(&s_cnt[e], 1);
+  // the slots are read in chunks of BK_PER per thread, all loads of a chunk
+  // in flight together (the rounds below take them from registers)
+  for (int64_t c0 = 0; c0 < F; c0 += BK_CHUNK) {
+    int ev[BK_PER];
+#pragma unroll
+    for (int i = 0; i < BK_PER; ++i) {
+      const int64_t f = c0 + (int64_t)i * BK_THREADS + tid;
+      ev[i] = f < F ? idx[f] : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < BK_PER; ++i)
+      if (ev[i] >= 0 && ev[i] < E) atomicAdd(&s_cnt[ev[i]], 1);
   }
   __syncthreads();
 
@@ -536,36 +547,46 @@ __device__ void bucket_block(int32_t T, int32_t K, int32_t E, const int32_t* idx
   // the same expert) and per-wave counts in LDS for earlier waves: no atomics
   // on positions, so the order is the stable one.
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int64_t r0 = 0; r0 < F; r0 += BK_THREADS) {
-    const int64_t f = r0 + tid;
-    const int e = f < F ? idx[f] : -1;
-    const bool valid = e >= 0 && e < E;
-    uint64_t m = __ballot(valid);
+  for (int64_t c0 = 0; c0 < F; c0 += BK_CHUNK) {
+    int ev[BK_PER];
 #pragma unroll
-    for (int b = 0; b < BK_KEY_BITS; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t bm = __ballot(bit);
-      m &= bit ? bm : ~bm;
+    for (int i = 0; i < BK_PER; ++i) {
+      const int64_t f = c0 + (int64_t)i * BK_THREADS + tid;
+      ev[i] = f < F ? idx[f] : -1;
     }
-    const int rank = __popcll(m & lt_mask);
-    const int cnt = __popcll(m);
-    const bool leader = valid && rank == 0;
-    if (leader) s_wcnt[wave][e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int pos = s_base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
-      entries[pos] = (int32_t)f;
-      inverse[f] = pos;
-    } else if (f < F) {
-      inverse[f] = -1;   // a dropped slot
+#pragma unroll
+    for (int i = 0; i < BK_PER; ++i) {
+      const int64_t f = c0 + (int64_t)i * BK_THREADS + tid;
+      if (c0 + (int64_t)i * BK_THREADS >= F) break;   // uniform: past the last round
+      const int e = ev[i];
+      const bool valid = e >= 0 && e < E;
+      uint64_t m = __ballot(valid);
+#pragma unroll
+      for (int b = 0; b < BK_KEY_BITS; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t bm = __ballot(bit);
+        m &= bit ? bm : ~bm;
+      }
+      const int rank = __popcll(m & lt_mask);
+      const int cnt = __popcll(m);
+      const bool leader = valid && rank == 0;
+      if (leader) s_wcnt[wave][e] = cnt;
+      __syncthreads();
+      if (valid) {
+        int pos = s_base[e] + rank;
+        for (int w = 0; w < wave; ++w) pos += s_wcnt[w][e];
+        entries[pos] = (int32_t)f;
+        inverse[f] = pos;
+      } else if (f < F) {
+        inverse[f] = -1;   // a dropped slot
+      }
+      __syncthreads();
+      if (leader) {
+        atomicAdd(&s_base[e], cnt);
+        s_wcnt[wave][e] = 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&s_base[e], cnt);
-      s_wcnt[wave][e] = 0;
-    }
-    __syncthreads();
   }
 }
 
