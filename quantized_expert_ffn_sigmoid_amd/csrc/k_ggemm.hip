@@ -377,6 +377,9 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 // Waits until at most N vector memory loads of this wave are outstanding.
 // The asm form keeps memory accesses from moving across the wait; the
 // builtin repeats it in a form the compiler's own wait insertion sees.
+// The counts assume that the only vector memory instructions in flight are
+// the pipeline's own loads; the built code holds no register spills (scratch
+// accesses) between a tile's first direct load and its final wait.
 template <int N>
 __device__ __forceinline__ void gg_wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
