@@ -86,11 +86,15 @@ __device__ __forceinline__ bool gg_tile(const GgArgs& a, GgTile& t) {
     const int64_t q = j / a.nt_r;
     t.nt = (int)(j - q * a.nt_r);
     const int mt = x + 8 * (int)q;
-    if (mt >= *a.n_tiles) return false;
+    // the record is read together with the count (one round trip), from a
+    // clamped index that stays inside the tile arrays
+    const int mtc = min(mt, a.max_tiles - 1);
+    const int used = *a.n_tiles;
+    t.e = a.tile_e[mtc];
+    t.p0 = a.tile_p0[mtc];
+    t.n = a.tile_n[mtc];
+    if (mt >= used) return false;
     t.shared = false;
-    t.e = a.tile_e[mt];
-    t.p0 = a.tile_p0[mt];
-    t.n = a.tile_n[mt];
   } else {
     if (a.s_tiles == 0 || a.nt_s == 0) return false;
     const int64_t j2 = j - rq * a.nt_r;
@@ -445,21 +449,16 @@ __device__ __forceinline__ void gg_run_lds(const GgArgs& a, const GgTile& t, uin
   // position l & 15, which holds logical piece (l & 15) ^ (row % 16).
   const int xp = lane & 15, xr = 4 * wave + (lane >> 4);
   const int xc = xp ^ xr;
-  const uint8_t* xsrc[MS];
+  // the rows' sources: for routed gate/up tiles the bucket entries, read
+  // before the first weights so that the two latencies overlap
+  int src[MS];
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    const int rr = min(xr + 16 * i, t.n - 1);
-    const uint16_t* row;
-    if (DOWN) {
-      row = (t.shared ? a.h_s : a.h) + (int64_t)(t.p0 + rr) * K;
-    } else {
-      const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
-      row = a.x_p + (int64_t)tok * K;
-    }
-    xsrc[i] = reinterpret_cast<const uint8_t*>(row) + xc * 16;
+    const int pos = t.p0 + min(xr + 16 * i, t.n - 1);
+    src[i] = (DOWN || t.shared) ? pos : a.entries[pos];
   }
   const int nk = K / GG_BK;
-  auto issue_x = [&](int kt, int stage) {
+  auto issue_x = [&](int kt, int stage, const uint8_t* const (&xsrc)[MS]) {
 #pragma unroll
     for (int i = 0; i < MS; ++i)
       __builtin_amdgcn_global_load_lds(xsrc[i] + (int64_t)kt * (GG_BK * 2),
@@ -471,15 +470,30 @@ __device__ __forceinline__ void gg_run_lds(const GgArgs& a, const GgTile& t, uin
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) v[ns] = *reinterpret_cast<const u32x4g*>(wp[ns] + (int64_t)kt * 64);
   };
+  // The first step's weights, then the activation rows' addresses (a wait
+  // for the entries only), then the first step's activations and the next
+  // steps' activations and weights: loads complete in issue order, and from
+  // x(0) on the sequence is the loop's, x(j) then w(j) (the first step's
+  // weights only come earlier), so every step's wait has the same count.
+  issue_w(0, wbuf[0]);
+  const uint8_t* xsrc[MS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i) {
+    const uint16_t* row;
+    if (DOWN) row = (t.shared ? a.h_s : a.h) + (int64_t)src[i] * K;
+    else row = a.x_p + (int64_t)(t.shared ? src[i] : src[i] / a.top_k) * K;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(row) + xc * 16;
+  }
 
   f32x4 acc[MS][4];
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
+  issue_x(0, 0, xsrc);
 #pragma unroll
-  for (int j = 0; j < D; ++j) {
-    issue_x(min(j, nk - 1), j);
+  for (int j = 1; j < D; ++j) {
+    issue_x(min(j, nk - 1), j, xsrc);
     issue_w(min(j, nk - 1), wbuf[j]);
   }
   if (threadIdx.x < GG_BM) {
@@ -493,7 +507,7 @@ __device__ __forceinline__ void gg_run_lds(const GgArgs& a, const GgTile& t, uin
       const int kt = kt0 + st;
       gg_wait_vm<(D - 1) * (MS + 4)>();
       gg_barrier();
-      issue_x(min(kt + D, nk - 1), (st + D) % S);
+      issue_x(min(kt + D, nk - 1), (st + D) % S, xsrc);
       issue_w(min(kt + D, nk - 1), wbuf[(st + D) % S]);
       if (kt < nk) {
         const uint8_t* xs = lds + st * GG_XSTAGE;
