@@ -261,19 +261,24 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
   // order (x_p, and h as gate/up writes it).
   const int xp = threadIdx.x & 15, xrb = threadIdx.x >> 4;
   const int xc = xp ^ xrb;   // logical piece
-  const uint8_t* xsrc[MS];
+  // the rows' sources: for routed gate/up tiles the bucket entries, read
+  // before the first weights so that the two latencies overlap
+  int src[MS];
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
-    const int rr = min(xrb + 16 * i, t.n - 1);
-    const uint16_t* row;
-    if (DOWN) {
-      row = (t.shared ? a.h_s : a.h) + (int64_t)(t.p0 + rr) * K;
-    } else {
-      const int tok = t.shared ? t.p0 + rr : a.entries[t.p0 + rr] / a.top_k;
-      row = (I4 ? a.x_p : a.x) + (int64_t)tok * K;
-    }
-    xsrc[i] = reinterpret_cast<const uint8_t*>(row) + (xc >> 2) * (64 * GRP) + (xc & 3) * 16;
+    const int pos = t.p0 + min(xrb + 16 * i, t.n - 1);
+    src[i] = (DOWN || t.shared) ? pos : a.entries[pos];
   }
+  const uint8_t* xsrc[MS];
+  auto make_xsrc = [&]() {
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const uint16_t* row;
+      if (DOWN) row = (t.shared ? a.h_s : a.h) + (int64_t)src[i] * K;
+      else row = (I4 ? a.x_p : a.x) + (int64_t)(t.shared ? src[i] : src[i] / a.top_k) * K;
+      xsrc[i] = reinterpret_cast<const uint8_t*>(row) + (xc >> 2) * (64 * GRP) + (xc & 3) * 16;
+    }
+  };
   const int nk = K / GG_BK;
   auto load_x = [&](int kt, u32x4g (&v)[MS]) {
     const int64_t off = (int64_t)(kt / GRP) * (256 * GRP) + (kt % GRP) * 64;
@@ -306,16 +311,18 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgTile& t, uint8_t
 #pragma unroll
     for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: activation sets of steps 0 .. XD - 1, the first NW weight
-  // steps, step 0 into stage 0 and its register set refilled with step XD
+  // prologue: the first NW weight steps, activation sets of steps 0 ..
+  // XD - 1, step 0 into stage 0 and its register set refilled with step XD
   constexpr int NWB = NW / GRP;   // weight register groups
+  // (the weights first: they do not wait for the bucket entries)
   u32x4g xr[XD][MS];
   u32x4g wbuf[NWB][4][WV];
 #pragma unroll
-  for (int j = 0; j < XD; ++j) load_x(min(j, nk - 1), xr[j]);
-#pragma unroll
   for (int st = 0; st < NW; ++st)
     if (st % GRP == GRP - 1) load_w(min(st, nk - 1), wbuf[st / GRP]);
+  make_xsrc();
+#pragma unroll
+  for (int j = 0; j < XD; ++j) load_x(min(j, nk - 1), xr[j]);
   store_x(0, xr[0]);
   load_x(min(XD, nk - 1), xr[0]);
   if (threadIdx.x < GG_BM) {
