@@ -188,10 +188,12 @@ def test_route_exact_ties(name):
         assert np.array_equal(idx, ridx)
 
 
+# (5000, 8, 256): 40000 slots, more than one chunk of the 1024-thread block's
+# read-ahead (16 slots per thread) and a ragged last round
 BUCKET_CASES = [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (7, 2, 8), (33, 5, 1000), (0, 8, 256),
-                (1, 1, 1), (300, 4, 3)]
+                (1, 1, 1), (300, 4, 3), (5000, 8, 256)]
 # slots dropped by adaptive top-p (index -1): small and large slot counts
-BUCKET_DROP_CASES = [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (33, 5, 1000)]
+BUCKET_DROP_CASES = [(1, 8, 256), (16, 8, 256), (2048, 8, 256), (33, 5, 1000), (3000, 8, 256)]
 
 
 @pytest.mark.parametrize("T,K,E", BUCKET_DROP_CASES)
