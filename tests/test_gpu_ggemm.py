@@ -4,7 +4,8 @@ Batches above the decode size with bf16 activations run the expert FFNs as a
 grouped GEMM over 64-row bucket tiles.  These cases compare every output of
 the layer with the oracle on small layers whose buckets span several tiles,
 ragged last tiles and tiles of one row, for int4 and bf16 routed experts and
-int4, bf16 or no shared expert, with n-tile counts from 1 to 8.  The GLM-scale prefill case lives in
+int4, bf16 or no shared expert, with n-tile counts from 1 to 8 and up to 583
+560 active experts.  The GLM-scale prefill case lives in
 test_gpu_layer.py (sampled tokens).
 """
 import numpy as np
@@ -47,6 +48,10 @@ def _cfg(kind):
     if kind == "i4_xcd_i4shared":
         return gen.shrink(base, **dict(small, hidden=2048, inter=1024, shared_dtype=gen.I4,
                                        seed=37))
+    if kind == "i4_many":
+        # more active experts than one thread of the tile-list scan takes
+        # (600 experts, 583 active)
+        return gen.shrink(base, **dict(small, n_experts=600, top_k=8, seed=38))
     if kind == "bf16":
         return gen.shrink(base, hidden=256, inter=128, n_experts=8, top_k=2, n_group=2,
                           topk_group=1, expert_dtype=gen.BF16, shared_dtype=gen.BF16,
@@ -56,7 +61,7 @@ def _cfg(kind):
 
 CASES = [("i4_bf16shared", 17), ("i4_bf16shared", 100), ("i4_bf16shared", 300),
          ("i4_i4shared", 70), ("i4_noshared", 65), ("i4_zipf", 400), ("i4_odd_k", 50),
-         ("i4_topp", 120), ("i4_xcd", 150), ("i4_xcd_i4shared", 90),
+         ("i4_topp", 120), ("i4_xcd", 150), ("i4_xcd_i4shared", 90), ("i4_many", 300),
          ("bf16", 40), ("bf16", 129)]
 
 
