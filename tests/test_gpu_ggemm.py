@@ -5,8 +5,8 @@ grouped GEMM over 64-row bucket tiles.  These cases compare every output of
 the layer with the oracle on small layers whose buckets span several tiles,
 ragged last tiles and tiles of one row, for int4 and bf16 routed experts and
 int4, bf16 or no shared expert, with n-tile counts from 1 to 8 and up to 583
-560 active experts.  The GLM-scale prefill case lives in
-test_gpu_layer.py (sampled tokens).
+active experts.  The GLM-scale prefill case lives in test_gpu_layer.py
+(sampled tokens).
 """
 import numpy as np
 import pytest
