@@ -645,10 +645,13 @@ __device__ __forceinline__ void stage_wave_scales(const Job& jb, int nr, int wav
 // The wave's rows of the block: local rows wave, wave + kWaves, ... < nr.
 // Row results (scaled, SwiGLU applied for PAIR) go to L.out[n][local row].
 // Activation rows are read sliced, or staged through the ring area before the
-// ring starts; every wave of the block calls this together.
-template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED>
-__device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff, int nt,
-                         RingLds& L) {
+// ring starts, or (PRE) were read by the caller, who passes the slices and
+// their granule sums in xpre / gpre: then the whole first fill is issued at
+// once.  Every wave of the block calls this together.
+template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED, bool PRE = false>
+__device__ __forceinline__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff,
+                                         int nt, RingLds& L, const float* xpre = nullptr,
+                                         const float* gpre = nullptr) {
   using F = Fmt<WDT>;
   using RS = RingStream<WDT, KSL, PAIR>;
   constexpr int EPG = F::EPG, GB = F::GB, GPL = KSL / EPG;
@@ -668,7 +671,16 @@ __device__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* 
   // activations (waited for at once), then the rest of the ring's first fill
   if constexpr (WDT != MOE_BF16) stage_wave_scales<PAIR>(jb, nr, wave, L);
   float x[NT][KSL], gs[NT][GPL];
-  if constexpr (!SLICED) {
+  if constexpr (PRE) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+      for (int k = 0; k < KSL; ++k) x[n][k] = xpre[n * KSL + k];
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) gs[n][g] = gpre[n * GPL + g];
+    }
+    st.template prologue<0, kRing>();
+  } else if constexpr (!SLICED) {
     // the ring area stages the activation rows first
     slices_via_lds<EPG, KSL, NT, ABF16>(src, xoff, nt, jb.K, &L.ring[0][0][0], x, gs);
     st.template prologue<0, kRing>();
@@ -902,8 +914,12 @@ __device__ __forceinline__ Job make_job(const GemvArgs& a, const BlockWork& bw, 
   return jb;
 }
 
-template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN>
-__device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
+// PRE: one routed gate/up row on the ring path whose activation slice and
+// granule sums the caller has read already (xpre / gpre, as job_ring takes them).
+template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN, bool PRE = false>
+__device__ __forceinline__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L,
+                                          const float* xpre = nullptr, const float* gpre = nullptr) {
+  static_assert(!PRE || (NTMAX == 1 && !DOWN), "preloaded slices: one gate/up row at a time");
   const Job jb = make_job(a, bw, DOWN);
   if (jb.r0 >= jb.rows) return;
   const RowSource& src = a.src;
@@ -945,7 +961,9 @@ __device__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L) {
     }
     if constexpr (kRingFmt) {
       if (ring) {
-        if (a.in_sliced) {
+        if constexpr (PRE) {
+          job_ring<WDT, KSL, 1, ABF16, !DOWN, true, true>(jb, nr, in, xo, 1, L, xpre, gpre);
+        } else if (a.in_sliced) {
           if (NT2 == 2 && nt >= 2)
             job_ring<WDT, KSL, NT2, ABF16, !DOWN, true>(jb, nr, in, xo, nt, L);
           else

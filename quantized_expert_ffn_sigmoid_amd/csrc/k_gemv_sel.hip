@@ -41,6 +41,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   __shared__ RingLds lds;
   SelScratch& S = *reinterpret_cast<SelScratch*>(&lds.ring[0][0][0]);
   const int T = p.T, F = T * p.sp.K, E = p.sp.E;
+  // The token's activation slice (sliced row 0: every routed row of a
+  // one-token step is token 0) does not depend on the routing: its loads go
+  // out before the selection, so that they have landed when the block's ring
+  // starts, and the ring's whole first fill is issued at once.
+  constexpr int GPL = KR / Fmt<WR>::EPG;
+  float xpre[KR], gpre[GPL];
+  {
+    const int64_t xo0 = 0;
+    float (&xv)[1][KR] = *reinterpret_cast<float (*)[1][KR]>(&xpre[0]);
+    slices_sliced_load<Fmt<WR>::EPG, KR, 1, ABF16>(a.x, &xo0, 1, xv);
+  }
   SlotTables tb;
   tb.slot_tab = S.slot_tab;
   tb.n_tab = p.tb.n_tab;
@@ -83,7 +94,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   // every wave holds its record before the ring overwrites the scratch
   __syncthreads();
   if (!ok) return;
-  run_block<WR, KR, 1, ABF16, false>(b, bw, lds);
+  {
+    float (&xv)[1][KR] = *reinterpret_cast<float (*)[1][KR]>(&xpre[0]);
+    float (&gv)[1][GPL] = *reinterpret_cast<float (*)[1][GPL]>(&gpre[0]);
+    slice_finish<Fmt<WR>::EPG, KR, 1, ABF16>(xv, gv);
+  }
+  run_block<WR, KR, 1, ABF16, false, true>(b, bw, lds, xpre, gpre);
 }
 
 template <int WR, int KR, int EPL>
