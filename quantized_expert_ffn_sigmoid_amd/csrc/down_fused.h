@@ -237,15 +237,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   int ue[2] = {0, 0}, uh[2] = {0, 0};
   float uw[2] = {0.f, 0.f};
   int nu = 0;
+  if (a.n_slots > 0) {
+    // one round trip: lanes 0 and 1 read the two records (indexes clamped
+    // to a record that exists), every lane a routing weight of the token (a
+    // one-token step's record names its weight by its flat slot, < n_slots);
+    // a record past the active experts holds only its expert field, -1
+    const int su = min(wave + (lane & 1) * kWaves, a.n_slots - 1);
+    const int4 rv = *reinterpret_cast<const int4*>(a.slot_tab + (int64_t)su * kSlotRec);
+    const float wl = a.topk_w[min(lane, a.n_slots - 1)];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int s = wave + u * kWaves;
-    if (s < a.n_slots) {
-      const int4 rec = *reinterpret_cast<const int4*>(a.slot_tab + (int64_t)s * kSlotRec);
-      if (rec.x >= 0 && nu == u) {
-        ue[u] = rec.x;
-        uh[u] = rec.y;
-        uw[u] = a.topk_w[rec.w];
+    for (int u = 0; u < 2; ++u) {
+      const int rx = __builtin_amdgcn_readlane(rv.x, u);
+      const int ry = __builtin_amdgcn_readlane(rv.y, u);
+      const int rw = min(max(__builtin_amdgcn_readlane(rv.w, u), 0), a.n_slots - 1);
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), rw));
+      if (wave + u * kWaves < a.n_slots && rx >= 0 && nu == u) {
+        ue[u] = rx;
+        uh[u] = ry;
+        uw[u] = w;
         nu = u + 1;
       }
     }
