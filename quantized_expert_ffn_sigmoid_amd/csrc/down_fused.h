@@ -45,21 +45,42 @@ struct DownFusedArgs {
   float* y_copy;             // nullable: y (the layer output without residual)
 };
 
-// Loads GS granules of the sliced activation row, starting at granule g0 of
-// the lane's slice (lane j's granule g holds elements (g * 64 + j) * EPG ..).
+// Pieces of 16 bytes per lane that hold NG granules of a sliced activation
+// row (fp32 or bf16 activations, EPG elements per granule).
 template <int EPG, int NG, int ABF16>
-__device__ __forceinline__ void fused_slice_load(const void* src, int g0, float (&x)[NG * EPG],
-                                                 float (&gs)[NG]) {
-  constexpr int AB = ABF16 ? 2 : 4, P = 16 / AB, PPC = EPG / P;
+constexpr int slice_pieces() {
+  return NG * (EPG / (16 / (ABF16 ? 2 : 4)));
+}
+
+// Loads NG granules of the sliced activation row, starting at granule g0 of
+// the lane's slice (lane j's granule g holds elements (g * 64 + j) * EPG ..),
+// as raw pieces: the loads only, so that the caller can issue more loads
+// before the first use of these.
+template <int EPG, int NG, int ABF16>
+__device__ __forceinline__ void slice_raw_load(const void* src, int g0,
+                                               u32x4 (&raw)[slice_pieces<EPG, NG, ABF16>()]) {
+  constexpr int PPC = slice_pieces<EPG, 1, ABF16>();
   const int j = threadIdx.x & 63;
   const uint8_t* row = reinterpret_cast<const uint8_t*>(src);
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int c = 0; c < PPC; ++c)
+      raw[g * PPC + c] =
+          *reinterpret_cast<const u32x4*>(row + ((int64_t)((g0 + g) * PPC + c) * 64 + j) * 16);
+}
+
+// The activations of the raw pieces as floats, and each granule's sum.
+template <int EPG, int NG, int ABF16>
+__device__ __forceinline__ void slice_raw_finish(const u32x4 (&raw)[slice_pieces<EPG, NG, ABF16>()],
+                                                 float (&x)[NG * EPG], float (&gs)[NG]) {
+  constexpr int PPC = slice_pieces<EPG, 1, ABF16>();
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     float s = 0.f;
 #pragma unroll
     for (int c = 0; c < PPC; ++c) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(
-          row + ((int64_t)((g0 + g) * PPC + c) * 64 + j) * 16);
+      const u32x4 v = raw[g * PPC + c];
       if constexpr (ABF16) {
         const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -85,9 +106,10 @@ __device__ __forceinline__ void fused_slice_load(const void* src, int g0, float 
 // granules of every block row.  Items of row i, in order: the slots of unit
 // 0's row (granule-major, int8 halves inner), unit 1's, then the shared
 // granules; ring slot n holds item n.
-template <int WR, int KR, int WS, int GS, int NU, int ABF16>
+template <int WR, int KR, int WS, int GS, int NU, int ABF16, int PR, int PS>
 __device__ void fused_wave(const DownFusedArgs& a, int o0, int R, FusedLds& L, const int (&ue)[2],
-                           const int (&uh)[2], const float (&uw)[2]) {
+                           const float (&uw)[2], const u32x4 (&hraw)[2][PR],
+                           const u32x4 (&sraw)[PS]) {
   using FR = Fmt<WR>;
   using FS = Fmt<WS>;
   constexpr int GPL = KR / FR::EPG;
@@ -130,33 +152,21 @@ __device__ void fused_wave(const DownFusedArgs& a, int o0, int R, FusedLds& L, c
     __builtin_amdgcn_global_load_lds(p, (lds_ptr_t)(ring + (n & (kRing - 1)) * 1024), 16, 0, 2);
   };
 
-  // activations: the units' h rows and the wave's granules of h_s
+  // activations: the units' h rows and the wave's granules of h_s, loaded
+  // by the caller (they have landed); the ring's whole first fill goes out
   float xr[NU > 0 ? NU : 1][KR], gr[NU > 0 ? NU : 1][GPL];
   float xs[GS > 0 ? GS * FS::EPG : 1], gss[GS > 0 ? GS : 1];
+  static_assert(PR == slice_pieces<FR::EPG, GPL, ABF16>(), "routed h pieces");
 #pragma unroll
-  for (int n = 0; n < kRingPre; ++n) issue(n);
-  constexpr int ABR = ABF16 ? 2 : 4;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    // the unit's h row (its bucket position)
-    const uint8_t* hrow = reinterpret_cast<const uint8_t*>(a.h) + (int64_t)uh[u] * a.I * ABR;
-    fused_slice_load<FR::EPG, GPL, ABF16>(hrow, 0, xr[u], gr[u]);
-  }
+  for (int u = 0; u < NU; ++u) slice_raw_finish<FR::EPG, GPL, ABF16>(hraw[u], xr[u], gr[u]);
   if constexpr (GS > 0) {
+    static_assert(PS == slice_pieces<FS::EPG, GS, ABF16>(), "shared h pieces");
     float (&xsv)[GS * FS::EPG] = *reinterpret_cast<float (*)[GS * FS::EPG]>(&xs[0]);
     float (&gsv)[GS] = *reinterpret_cast<float (*)[GS]>(&gss[0]);
-    fused_slice_load<FS::EPG, GS, ABF16>(a.h_s, wave * GS, xsv, gsv);
+    slice_raw_finish<FS::EPG, GS, ABF16>(sraw, xsv, gsv);
   }
 #pragma unroll
-  for (int u = 0; u < NU; ++u)
-#pragma unroll
-    for (int g = 0; g < GPL; ++g) asm volatile("" : "+v"(gr[u][g]) : : "memory");
-  if constexpr (GS > 0) {
-#pragma unroll
-    for (int g = 0; g < GS; ++g) asm volatile("" : "+v"(gss[g]) : : "memory");
-  }
-#pragma unroll
-  for (int n = kRingPre; n < kRing; ++n) issue(n);
+  for (int n = 0; n < kRing; ++n) issue(n);
 
   auto read_slot = [&](int n) {
     return *reinterpret_cast<const u32x4*>(ring + (n & (kRing - 1)) * 1024 + lane * 16);
@@ -237,6 +247,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   int ue[2] = {0, 0}, uh[2] = {0, 0};
   float uw[2] = {0.f, 0.f};
   int nu = 0;
+  // The h rows go out first: a one-token step's grouping gives every active
+  // expert one row, in expert order, so slot s's row is bucket position s
+  // (checked against the records below).  Clamped to a row that exists.
+  using FR = Fmt<WR>;
+  constexpr int GPL = KR / FR::EPG;
+  constexpr int PR = slice_pieces<FR::EPG, GPL, ABF16>();
+  constexpr int PS = GS > 0 ? slice_pieces<Fmt<WS>::EPG, GS, ABF16>() : 1;
+  constexpr int ABR = ABF16 ? 2 : 4;
+  const int last = max(a.n_slots, 1) - 1;
+  u32x4 hraw[2][PR], sraw[PS];
+  auto load_h = [&](int u, int pos) {
+    slice_raw_load<FR::EPG, GPL, ABF16>(
+        reinterpret_cast<const uint8_t*>(a.h) + (int64_t)pos * a.I * ABR, 0, hraw[u]);
+  };
+#pragma unroll
+  for (int u = 0; u < 2; ++u) load_h(u, min(wave + u * kWaves, last));
+  if constexpr (GS > 0) slice_raw_load<Fmt<WS>::EPG, GS, ABF16>(a.h_s, wave * GS, sraw);
   if (a.n_slots > 0) {
     // one round trip: lanes 0 and 1 read the two records (indexes clamped
     // to a record that exists), every lane a routing weight of the token (a
@@ -266,6 +293,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     uw[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(uw[u])));
   }
   nu = __builtin_amdgcn_readfirstlane(nu);
+  // a record whose row is not at its slot's position (not a one-token
+  // grouping): that row again, from where the record puts it
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (u < nu && uh[u] != wave + u * kWaves) load_h(u, uh[u]);
   // row scales of the wave's units, by direct loads into LDS (lane l fills
   // entry l; lanes past the block's rows reload its last row); the ring's
   // first wait covers them, as they are issued before its loads
@@ -276,9 +308,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
                                        (lds_ptr_t)&L.scale[wave + u * kWaves][0], 4, 0, 0);
     }
   }
-  if (nu == 2) fused_wave<WR, KR, WS, GS, 2, ABF16>(a, o0, R, L, ue, uh, uw);
-  else if (nu == 1) fused_wave<WR, KR, WS, GS, 1, ABF16>(a, o0, R, L, ue, uh, uw);
-  else fused_wave<WR, KR, WS, GS, 0, ABF16>(a, o0, R, L, ue, uh, uw);
+  if (nu == 2) fused_wave<WR, KR, WS, GS, 2, ABF16, PR, PS>(a, o0, R, L, ue, uw, hraw, sraw);
+  else if (nu == 1) fused_wave<WR, KR, WS, GS, 1, ABF16, PR, PS>(a, o0, R, L, ue, uw, hraw, sraw);
+  else fused_wave<WR, KR, WS, GS, 0, ABF16, PR, PS>(a, o0, R, L, ue, uw, hraw, sraw);
   __syncthreads();
   for (int r = threadIdx.x; r < R; r += kThreads) {
     float y = L.part[0][r];
