@@ -524,6 +524,34 @@ __device__ __forceinline__ void slices_sliced_load(const void* src, const int64_
   }
 }
 
+// Activation slices read from rows in natural order: lane j's piece c of
+// granule g is the 16 bytes at ((g * 64 + j) * PPC + c) * 16, so one load
+// instruction of the wave spans the 64 granules of one row segment (every
+// wave of a block reads the whole row; it stays in the caches).  The loads
+// only, with the register layout of slices_sliced_load.
+template <int EPG, int KSL, int NT, int ABF16>
+__device__ __forceinline__ void slices_natural_load(const void* src, const int64_t* xoff, int nt,
+                                                    float (&x)[NT][KSL]) {
+  constexpr int AB = ABF16 ? 2 : 4, P = 16 / AB, PPC = EPG / P, GPL = KSL / EPG;
+  const int j = threadIdx.x & 63;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const uint8_t* row = reinterpret_cast<const uint8_t*>(src) + xoff[n < nt ? n : 0] * AB;
+#pragma unroll
+    for (int g = 0; g < GPL; ++g) {
+#pragma unroll
+      for (int c = 0; c < PPC; ++c) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(row + ((int64_t)(g * 64 + j) * PPC + c) * 16);
+        const int b = ABF16 ? g * EPG + c * 8 : g * EPG + c * 4;
+        x[n][b] = __uint_as_float(v.x);
+        x[n][b + 1] = __uint_as_float(v.y);
+        x[n][b + 2] = __uint_as_float(v.z);
+        x[n][b + 3] = __uint_as_float(v.w);
+      }
+    }
+  }
+}
+
 // Widens packed bf16 pieces (bf16 rows) and forms the granule sums.
 template <int EPG, int KSL, int NT, int ABF16>
 __device__ __forceinline__ void slice_finish(float (&x)[NT][KSL], float (&gs)[NT][KSL / EPG]) {
@@ -647,8 +675,11 @@ __device__ __forceinline__ void stage_wave_scales(const Job& jb, int nr, int wav
 // Activation rows are read sliced, or staged through the ring area before the
 // ring starts, or (PRE) were read by the caller, who passes the slices and
 // their granule sums in xpre / gpre: then the whole first fill is issued at
-// once.  Every wave of the block calls this together.
-template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED, bool PRE = false>
+// once.  NATX (rows in natural order): the wave reads its slices with
+// register loads, issues the whole first fill behind them and waits for the
+// activations only.  Every wave of the block calls this together.
+template <int WDT, int KSL, int NT, int ABF16, bool PAIR, bool SLICED, bool PRE = false,
+          bool NATX = false>
 __device__ __forceinline__ void job_ring(const Job& jb, int nr, const void* src, const int64_t* xoff,
                                          int nt, RingLds& L, const float* xpre = nullptr,
                                          const float* gpre = nullptr) {
@@ -680,6 +711,12 @@ __device__ __forceinline__ void job_ring(const Job& jb, int nr, const void* src,
       for (int g = 0; g < GPL; ++g) gs[n][g] = gpre[n * GPL + g];
     }
     st.template prologue<0, kRing>();
+  } else if constexpr (NATX) {
+    slices_natural_load<EPG, KSL, NT, ABF16>(src, xoff, nt, x);
+    st.template prologue<0, kRing>();
+    // the activation loads, issued before the ring's kRing, have landed
+    wait_vmcnt<kRing>();
+    slice_finish<EPG, KSL, NT, ABF16>(x, gs);
   } else if constexpr (!SLICED) {
     // the ring area stages the activation rows first
     slices_via_lds<EPG, KSL, NT, ABF16>(src, xoff, nt, jb.K, &L.ring[0][0][0], x, gs);
@@ -916,7 +953,9 @@ __device__ __forceinline__ Job make_job(const GemvArgs& a, const BlockWork& bw, 
 
 // PRE: one routed gate/up row on the ring path whose activation slice and
 // granule sums the caller has read already (xpre / gpre, as job_ring takes them).
-template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN, bool PRE = false>
+// NATX: input rows in natural order are read by job_ring's NATX mode instead
+// of being staged through the ring area.
+template <int WDT, int KSL, int NTMAX, int ABF16, bool DOWN, bool PRE = false, bool NATX = false>
 __device__ __forceinline__ void run_block(const GemvArgs& a, BlockWork bw, RingLds& L,
                                           const float* xpre = nullptr, const float* gpre = nullptr) {
   static_assert(!PRE || (NTMAX == 1 && !DOWN), "preloaded slices: one gate/up row at a time");
@@ -968,6 +1007,11 @@ __device__ __forceinline__ void run_block(const GemvArgs& a, BlockWork bw, RingL
             job_ring<WDT, KSL, NT2, ABF16, !DOWN, true>(jb, nr, in, xo, nt, L);
           else
             job_ring<WDT, KSL, 1, ABF16, !DOWN, true>(jb, nr, in, xo, 1, L);
+        } else if constexpr (NATX) {
+          if (NT2 == 2 && nt >= 2)
+            job_ring<WDT, KSL, NT2, ABF16, !DOWN, false, false, true>(jb, nr, in, xo, nt, L);
+          else
+            job_ring<WDT, KSL, 1, ABF16, !DOWN, false, false, true>(jb, nr, in, xo, 1, L);
         } else {
           if (NT2 == 2 && nt >= 2)
             job_ring<WDT, KSL, NT2, ABF16, !DOWN, false>(jb, nr, in, xo, nt, L);
@@ -1043,7 +1087,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
   BlockWork bw;
   if (!block_work(a, bw, (int64_t)blockIdx.x - p.blocks)) return;
-  run_block<WS, KS, 1, ABF16, DOWN>(a, bw, lds);
+  // the gate/up launch reads the layer input as it is: in natural order,
+  // with the weight ring's first fill issued behind the activation loads
+  run_block<WS, KS, 1, ABF16, DOWN, false, !DOWN>(a, bw, lds);
 }
 
 template <int WS, int KS, bool DOWN>
