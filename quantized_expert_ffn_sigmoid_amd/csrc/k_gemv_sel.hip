@@ -17,11 +17,11 @@ namespace moe {
 namespace {
 
 constexpr int kSelMaxSlots = kDecodeTokens * kMaxTopK;
+constexpr int kMaxSelExperts = 4 * 64;   // experts per lane (EPL) at most 4
 
 // The block's copy of the routing and grouping, in the ring area of the LDS
 // (dead once the block knows its slot, before the ring fills).
 struct __attribute__((aligned(16))) SelScratch {
-  SelectBucketLds sb;
   int32_t idx[kSelMaxSlots];
   float w[kSelMaxSlots];
   int32_t counts[kMaxExperts];
@@ -41,10 +41,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   __shared__ RingLds lds;
   SelScratch& S = *reinterpret_cast<SelScratch*>(&lds.ring[0][0][0]);
   const int T = p.T, F = T * p.sp.K, E = p.sp.E;
-  // The token's activation slice (sliced row 0: every routed row of a
-  // one-token step is token 0) does not depend on the routing: its loads go
-  // out before the selection, so that they have landed when the block's ring
-  // starts, and the ring's whole first fill is issued at once.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Wave 0 selects: its candidate loads go out first.  The token's
+  // activation slice (sliced row 0: every routed row of a one-token step is
+  // token 0) does not depend on the routing: its loads follow, so that they
+  // have landed when the block's ring starts, and the ring's whole first fill
+  // is issued at once.
+  double ra[EPL], rb[EPL];
+  if (wave == 0) {
+    if (p.sp.softmax) select_load<EPL, true>(p.sp, p.zin, p.bias, nullptr, ra, rb);
+    else select_load<EPL, false>(p.sp, p.zin, p.bias, p.sp.zsc, ra, rb);
+  }
   constexpr int GPL = KR / Fmt<WR>::EPG;
   float xpre[KR], gpre[GPL];
   {
@@ -56,8 +63,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   tb.slot_tab = S.slot_tab;
   tb.n_tab = p.tb.n_tab;
   tb.pos_e = S.pos_e;
-  select_bucket_block<EPL>(p.sp, p.zin, p.bias, T, S.idx, S.w, S.counts, S.offsets, S.entries,
-                           S.inverse, S.active, S.n_active, S.sb, tb);
+  if (wave == 0) {
+    // the selection and the grouping of the token, in this wave alone
+    if (p.sp.softmax) select_from<EPL, true>(p.sp, false, ra, rb, S.idx, S.w, nullptr);
+    else select_from<EPL, false>(p.sp, p.sp.zsc != nullptr, ra, rb, S.idx, S.w, nullptr);
+    bucket_one_token<(kMaxSelExperts + 63) / 64>(p.sp.K, E, S.idx, S.counts, S.offsets,
+                                                 S.entries, S.inverse, S.active, S.n_active, tb);
+  }
   __syncthreads();
   if (blockIdx.x == 0) {
     // the routing and the grouping for the caller and the later launches

@@ -185,39 +185,60 @@ __device__ __forceinline__ void segment_top2(double& a, double& b, int lpg) {
 // Wave-wide two largest values (a >= b); lanes hold their local (a, b).
 __device__ __forceinline__ void wave_top2(double& a, double& b) { segment_top2(a, b, 64); }
 
-// Selection for one token by one wave: zt = the token's E logits; writes its
-// k expert indices and weights (rank order) to idx_out / w_out, and the
-// indices also to idx_lds when given.  Lane l holds experts l*EPL ..
-// l*EPL+EPL-1, so a group is a run of consecutive lanes when EPL divides the
-// group size.  Closed (or absent) experts carry -inf; the candidate loops use
-// selects, and the loops over groups and ranks are wave-uniform.
+// The loads behind one token's selection candidates, issued but not used:
+// lane l reads experts l*EPL .. l*EPL+EPL-1 (clamped to the last expert):
+// the logits (softmax), the scores and biased scores the logits launch
+// formed (sct), or the logits and the bias.  A caller can issue other loads
+// before select_from consumes these.
 template <int EPL, bool SOFTMAX>
-__device__ __forceinline__ void select_token(const SelectParams& p, const double* __restrict__ zt,
-                                             const float* __restrict__ bias, int32_t* idx_out,
-                                             float* w_out, int32_t* idx_lds,
-                                             const double* sct = nullptr) {
+__device__ __forceinline__ void select_load(const SelectParams& p, const double* __restrict__ zt,
+                                            const float* __restrict__ bias, const double* sct,
+                                            double (&ra)[EPL], double (&rb)[EPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int ec = min(lane * EPL + i, p.E - 1);
+    if constexpr (SOFTMAX) {
+      ra[i] = zt[ec];
+      rb[i] = 0.0;
+    } else if (sct) {
+      ra[i] = sct[2 * ec];
+      rb[i] = sct[2 * ec + 1];
+    } else {
+      ra[i] = zt[ec];
+      rb[i] = bias ? (double)bias[ec] : 0.0;
+    }
+  }
+}
+
+// Selection for one token by one wave from the loads of select_load (sct:
+// whether they were scores); writes its k expert indices and weights (rank
+// order) to idx_out / w_out, and the indices also to idx_lds when given.
+// Lane l holds experts l*EPL .. l*EPL+EPL-1, so a group is a run of
+// consecutive lanes when EPL divides the group size.  Closed (or absent)
+// experts carry -inf; the candidate loops use selects, and the loops over
+// groups and ranks are wave-uniform.
+template <int EPL, bool SOFTMAX>
+__device__ __forceinline__ void select_from(const SelectParams& p, bool sct,
+                                            const double (&ra)[EPL], const double (&rb)[EPL],
+                                            int32_t* idx_out, float* w_out, int32_t* idx_lds) {
   const int lane = threadIdx.x & 63;
   const double NEG = -INFINITY;
   double c[EPL], sv[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    const int e = lane * EPL + i;
-    const bool ok = e < p.E;
-    const int ec = ok ? e : p.E - 1;
+    const bool ok = lane * EPL + i < p.E;
     if constexpr (SOFTMAX) {
-      const double zv = zt[ec];
-      sv[i] = zv;
-      c[i] = ok ? zv : NEG;
+      sv[i] = ra[i];
+      c[i] = ok ? ra[i] : NEG;
     } else if (sct) {
       // the token's scores, formed by the logits launch
-      sv[i] = sct[2 * ec];
-      c[i] = ok ? sct[2 * ec + 1] : NEG;
+      sv[i] = ra[i];
+      c[i] = ok ? rb[i] : NEG;
     } else {
-      const double zv = zt[ec];
-      const double s = 1.0 / (1.0 + exp(-zv));
+      const double s = 1.0 / (1.0 + exp(-ra[i]));
       sv[i] = s;
-      const double bb = bias ? (double)bias[ec] : 0.0;
-      c[i] = ok ? s + bb : NEG;
+      c[i] = ok ? s + rb[i] : NEG;
     }
   }
 
@@ -364,6 +385,18 @@ __device__ __forceinline__ void select_token(const SelectParams& p, const double
     w_out[lane] = keep ? (float)(my_s / kept_sum * (double)p.scaling) : 0.0f;
     if (idx_lds) idx_lds[lane] = keep ? my_idx : -1;
   }
+}
+
+// Selection for one token by one wave: zt = the token's E logits (or sct its
+// scores); select_load then select_from.
+template <int EPL, bool SOFTMAX>
+__device__ __forceinline__ void select_token(const SelectParams& p, const double* __restrict__ zt,
+                                             const float* __restrict__ bias, int32_t* idx_out,
+                                             float* w_out, int32_t* idx_lds,
+                                             const double* sct = nullptr) {
+  double ra[EPL], rb[EPL];
+  select_load<EPL, SOFTMAX>(p, zt, bias, sct, ra, rb);
+  select_from<EPL, SOFTMAX>(p, sct != nullptr, ra, rb, idx_out, w_out, idx_lds);
 }
 
 // -------------------------------------------------------------- grouping
@@ -678,6 +711,74 @@ __device__ __forceinline__ void logits_row_block(const float* __restrict__ W,
       zsc[((int64_t)tid * E + e) * 2] = s;
       zsc[((int64_t)tid * E + e) * 2 + 1] = s + (zbias ? (double)zbias[e] : 0.0);
     }
+  }
+}
+
+// The grouping of one token's k slots (the result bucket_small gives for
+// T = 1), by one wave with lane reads and no block barrier: the slots hold
+// distinct experts (or -1, dropped), so slot j's bucket position is the
+// number of kept slots with a smaller expert, every active expert has one
+// row, and a kept expert's place in the active list is its position.  idx:
+// the k expert indices (read by lanes < k, k <= 64); experts e = lane + 64 q
+// (q < EPE) cover all E.
+template <int EPE>
+__device__ __forceinline__ void bucket_one_token(int32_t K, int32_t E, const int32_t* idx,
+                                                 int32_t* __restrict__ counts,
+                                                 int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ entries,
+                                                 int32_t* __restrict__ inverse,
+                                                 int32_t* __restrict__ active,
+                                                 int32_t* __restrict__ n_active,
+                                                 const SlotTables& tb) {
+  const int lane = threadIdx.x & 63;
+  const int e0 = lane < K ? idx[lane] : -1;
+  const int key = (e0 >= 0 && e0 < E) ? e0 : -1;
+  const int nval = __popcll(__ballot(key >= 0));
+  int pos = 0, off[EPE], cnt[EPE];
+#pragma unroll
+  for (int q = 0; q < EPE; ++q) off[q] = cnt[q] = 0;
+  for (int i = 0; i < K; ++i) {
+    const int ki = __builtin_amdgcn_readlane(key, i);
+    if (ki < 0) continue;   // wave-uniform
+    pos += ki < key ? 1 : 0;
+#pragma unroll
+    for (int q = 0; q < EPE; ++q) {
+      const int e = lane + 64 * q;
+      off[q] += ki < e ? 1 : 0;
+      cnt[q] += ki == e ? 1 : 0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < EPE; ++q) {
+    const int e = lane + 64 * q;
+    if (e < E) {
+      counts[e] = cnt[q];
+      offsets[e] = off[q];
+    }
+  }
+  if (lane == 0) {
+    offsets[E] = nval;
+    n_active[0] = nval;
+  }
+  if (lane < K) {
+    inverse[lane] = key >= 0 ? pos : -1;
+    if (key >= 0) {
+      entries[pos] = lane;   // flat slot t * K + j of token 0
+      active[pos] = key;
+      if (tb.pos_e) tb.pos_e[pos] = key;
+      if (tb.slot_tab && pos < tb.n_tab) {
+        int32_t* r = tb.slot_tab + (int64_t)pos * kSlotRec;
+        r[0] = key;
+        r[1] = pos;
+        r[2] = 1;
+        r[3] = lane;
+        r[4] = -1;
+      }
+    }
+    // positions past the grouped slots hold no expert, nor records past the
+    // active experts
+    if (tb.pos_e && lane >= nval) tb.pos_e[lane] = -1;
+    if (tb.slot_tab && lane >= nval && lane < tb.n_tab) tb.slot_tab[(int64_t)lane * kSlotRec] = -1;
   }
 }
 
