@@ -131,10 +131,13 @@ __device__ __forceinline__ double key_value(uint64_t k) {
   return __longlong_as_double((long long)b);
 }
 
-// Wave-wide maximum of 32-bit unsigned values, in every lane.
+// Wave-wide maximum of 32-bit unsigned values, in every lane.  The lane
+// moves give every lane a valid source, so the move's old value (0, the
+// identity of the maximum) is never used; written this way the compiler
+// folds each move into the maximum that consumes it.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u<kDppXor1>(v));
