@@ -40,6 +40,8 @@ struct DownFusedArgs {
   const float* topk_w;       // [k] routing weights of the token
   const void* h;             // routed h rows [slot][I], sliced for the down matrix
   const void* h_s;           // shared h [Is], sliced for the shared down matrix
+  const float* s_pre;        // nullable: the shared expert's output [H], formed by the
+                             // gate/up launch (then no shared granules stream here)
   const float* residual;     // nullable: out = residual + y
   float* out;                // [H]
   float* y_copy;             // nullable: y (the layer output without residual)
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) y += L.part[w][r];
     const int o = o0 + r;
+    if (a.s_pre) y += a.s_pre[o];
     if (a.y_copy) a.y_copy[o] = y;
     a.out[o] = a.residual ? a.residual[o] + y : y;
   }

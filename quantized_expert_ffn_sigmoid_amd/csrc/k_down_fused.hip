@@ -47,6 +47,9 @@ hipError_t launch_down_fused(const moe_layer_desc& d, DownFusedArgs a, int act_b
                              hipStream_t s) {
   int kr, gs;
   if (!fused_geometry(d, kr, gs) || a.n_slots > kFusedMaxUnits) return hipErrorInvalidValue;
+  // the shared expert's output formed by the gate/up launch: only the routed
+  // rows stream here
+  if (a.s_pre) gs = 0;
   // rows per block: two blocks per CU over the output rows
   int R = (a.H + 511) / 512;
   if (R > kFusedMaxRows) R = kFusedMaxRows;

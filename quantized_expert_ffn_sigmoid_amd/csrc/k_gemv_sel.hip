@@ -10,7 +10,16 @@
 // own slot record there, and block 0 also writes the routing and grouping out
 // for the later launches and the caller.  No block reads another block's
 // writes, so no cross-block synchronisation is needed.
-#include "gemv_impl.h"
+//
+// While one wave selects, the block's other waves would idle for several
+// microseconds before any weight of the routed experts can be requested.
+// With a bf16 shared expert they spend that time on the shared expert's down
+// projection (its h is complete: the logits launch formed it), each block
+// over its share of the output rows, and the down launch adds that output
+// instead of streaming the shared weights itself.  Their loads go out after
+// the selecting wave's candidate loads (a barrier between the two), so that
+// the selection's inputs are not queued behind them.
+#include "down_fused.h"
 
 namespace moe {
 
@@ -35,7 +44,57 @@ struct __attribute__((aligned(16))) SelScratch {
 };
 static_assert(sizeof(SelScratch) <= sizeof(RingLds::ring), "selection scratch fits the ring area");
 
-template <int WR, int KR, int EPL, int ABF16>
+// The shared expert's down rows [o0, o1) of this block (o0 = block * rpb),
+// out[o] = sum_c down_s[o][c] h_s[c], by waves 1 .. kWaves - 1: wave w takes
+// rows o0 + w - 1, o0 + w - 1 + (kWaves - 1), ...  A lane holds granules j,
+// j + 64, j + 128, j + 192 of a kSdnIs-wide row (8 bf16 weights each) and the
+// matching 32 values of h; the rows of a pass are requested together, then
+// each is dotted, summed over the wave and written.
+template <int ABF16>
+__device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave) {
+  constexpr int EPG = Fmt<MOE_BF16>::EPG;
+  constexpr int GPL = kSdnIs / kWave / EPG;
+  constexpr int KSL = GPL * EPG;
+  constexpr int RW = 4;              // rows per pass
+  constexpr int NW = kWaves - 1;     // waves that take rows
+  constexpr int64_t RB = (int64_t)kSdnIs * 2;
+  static_assert(GPL * EPG * kWave == kSdnIs, "whole granules per lane");
+  const int lane = threadIdx.x & 63;
+  const int o0 = (int)blockIdx.x * p.sdn_rpb;
+  const int o1 = min(p.H, o0 + p.sdn_rpb);
+  if (o0 + wave - 1 >= o1) return;
+  const uint8_t* wl = p.sdn + lane * 16;
+  u32x4 hr[slice_pieces<EPG, GPL, ABF16>()];
+  slice_raw_load<EPG, GPL, ABF16>(p.sdn_h, 0, hr);
+  for (int r0 = o0 + wave - 1; r0 < o1; r0 += NW * RW) {
+    u32x4 v[RW][GPL];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int o = r0 + i * NW;   // wave-uniform
+#pragma unroll
+      for (int g = 0; g < GPL; ++g)
+        v[i][g] = o < o1 ? __builtin_nontemporal_load(
+                               reinterpret_cast<const u32x4*>(wl + (int64_t)o * RB + g * 1024))
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+    float x[1][KSL], gs[GPL];
+    slice_raw_finish<EPG, GPL, ABF16>(hr, x[0], gs);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int o = r0 + i * NW;
+      float acc[1] = {0.f};
+#pragma unroll
+      for (int g = 0; g < GPL; ++g) {
+        const uint32_t gr[4] = {v[i][g].x, v[i][g].y, v[i][g].z, v[i][g].w};
+        granule_fma<MOE_BF16, 1, KSL>(gr, x, g, acc);
+      }
+      const float sum = group_sum(acc[0], 64);
+      if (o < o1 && lane == 0) p.sdn_out[o] = sum;
+    }
+  }
+}
+
+template <int WR, int KR, int EPL, int ABF16, bool SDN>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_gemv_sel(
     GemvArgs a, PreArgs p) {
   __shared__ RingLds lds;
@@ -58,6 +117,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
     const int64_t xo0 = 0;
     float (&xv)[1][KR] = *reinterpret_cast<float (*)[1][KR]>(&xpre[0]);
     slices_sliced_load<Fmt<WR>::EPG, KR, 1, ABF16>(a.x, &xo0, 1, xv);
+  }
+  if constexpr (SDN) {
+    // wave 0's candidate loads are out before the other waves' shared rows
+    asm volatile("s_barrier" ::: "memory");
+    if (wave > 0) shared_down_rows<ABF16>(p, wave);
   }
   SlotTables tb;
   tb.slot_tab = S.slot_tab;
@@ -114,13 +178,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   run_block<WR, KR, 1, ABF16, false, true>(b, bw, lds, xpre, gpre);
 }
 
-template <int WR, int KR, int EPL>
-hipError_t go(const GemvArgs& a, const PreArgs& p, int act_bf16, unsigned blocks, hipStream_t s) {
+template <int WR, int KR, int EPL, bool SDN>
+hipError_t go2(const GemvArgs& a, const PreArgs& p, int act_bf16, unsigned blocks, hipStream_t s) {
   if (act_bf16)
-    hipLaunchKernelGGL((k_gemv_sel<WR, KR, EPL, 1>), dim3(blocks), dim3(kThreads), 0, s, a, p);
+    hipLaunchKernelGGL((k_gemv_sel<WR, KR, EPL, 1, SDN>), dim3(blocks), dim3(kThreads), 0, s, a, p);
   else
-    hipLaunchKernelGGL((k_gemv_sel<WR, KR, EPL, 0>), dim3(blocks), dim3(kThreads), 0, s, a, p);
+    hipLaunchKernelGGL((k_gemv_sel<WR, KR, EPL, 0, SDN>), dim3(blocks), dim3(kThreads), 0, s, a, p);
   return hipGetLastError();
+}
+
+template <int WR, int KR, int EPL>
+hipError_t go(const GemvArgs& a, PreArgs p, int act_bf16, unsigned blocks, hipStream_t s) {
+  if (!p.sdn) return go2<WR, KR, EPL, false>(a, p, act_bf16, blocks, s);
+  if (p.T != 1 || p.H <= 0 || !p.sdn_h || !p.sdn_out) return hipErrorInvalidValue;
+  p.sdn_rpb = (int)((p.H + blocks - 1) / blocks);
+  return go2<WR, KR, EPL, true>(a, p, act_bf16, blocks, s);
 }
 
 }  // namespace

@@ -292,6 +292,16 @@ moe_status layer_impl(const moe_layer_desc& d, const moe_layer_weights& w, const
     sel.active = active;
     sel.n_active = n_active;
     sel.tb = tb;
+    // a bf16 shared expert of intermediate size kSdnIs: its down projection
+    // runs in the gate/up launch, beside the selection, and the down launch
+    // adds its output
+    if (pre && has_sh && d.shared_dtype == MOE_BF16 && Ish == kSdnIs) {
+      sel.H = H;
+      sel.sdn = fa.ws.dn;
+      sel.sdn_h = h_sh;
+      sel.sdn_out = S;
+      fa.s_pre = S;
+    }
   }
 
   if (pre) {

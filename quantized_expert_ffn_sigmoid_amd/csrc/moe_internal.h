@@ -135,8 +135,16 @@ struct PreArgs {
   int32_t* active;
   int32_t* n_active;
   SlotTables tb;
+  // one-token gate/up launch only: the shared expert's down projection (bf16
+  // weights [H][Is], Is = kSdnIs), run by the waves that do not select; null
+  // when the down launch computes it
+  const uint8_t* sdn;
+  const void* sdn_h;    // the shared h, sliced for that matrix
+  float* sdn_out;       // [H] the shared expert's output
+  int32_t sdn_rpb;      // output rows per block (set by the launch)
 };
 constexpr int kPreLogits = 1, kPreSelect = 2;
+constexpr int kSdnIs = 2048;   // shared intermediate size of that variant
 
 // One GEMV launch: the routed experts of a bucket (or a fixed expert over a
 // row list) and, optionally, the shared expert over tokens 0..n_tok-1.
