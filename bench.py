@@ -170,10 +170,23 @@ def shared_runs_with_router(cfg, dtype, T):
             and _ring(cfg.shared_dtype, cfg.hidden) and _ring(cfg.shared_dtype, Is))
 
 
+def shared_down_in_gate_up(cfg, dtype, T):
+    """One-token decode whose gate/up launch selects in every block (the
+    integer GLM-scale layer, or a bf16 one of 1024 columns, with the router
+    beside the shared expert): with a bf16 shared expert of 2048 columns the
+    waves that do not select run the shared expert's down projection there."""
+    sel = ((dtype in (gen.I4, gen.I8) and cfg.hidden == 96 * 64 and 192 < cfg.n_experts <= 256)
+           or (dtype == gen.BF16 and cfg.hidden == 16 * 64 and cfg.n_experts <= 64))
+    return (T == 1 and sel and shared_runs_with_router(cfg, dtype, T)
+            and cfg.shared_dtype == gen.BF16 and cfg.inter * cfg.n_shared == 2048)
+
+
 def gate_up_bytes(cfg, dtype, n_active, T):
     """Algorithmic bytes of one gate/up launch: every active expert's gate/up
-    codes and scales once, the activations once, h written once; and the
-    shared expert's gate/up once when it shares the launch."""
+    codes and scales once, the activations once, h written once; the shared
+    expert's gate/up once when it shares the launch; and, when the launch
+    also runs the shared expert's down projection, its weights once, its h
+    read once and its output written once."""
     eb = expert_bytes(cfg, dtype)
     scale_bytes = 0 if dtype == gen.BF16 else 4 * 2 * cfg.inter
     act = 2 if cfg.act_dtype == gen.BF16 else 4
@@ -183,6 +196,9 @@ def gate_up_bytes(cfg, dtype, n_active, T):
         Is = cfg.inter * cfg.n_shared
         sb = gen.expert_bytes(cfg.shared_dtype, cfg.hidden, Is)
         b += sb["gate_up"] + (0 if cfg.shared_dtype == gen.BF16 else 4 * 2 * Is) + T * Is * act
+    if shared_down_in_gate_up(cfg, dtype, T):
+        Is = cfg.inter * cfg.n_shared
+        b += gen.expert_bytes(cfg.shared_dtype, cfg.hidden, Is)["down"] + Is * act + cfg.hidden * 4
     return b
 
 
@@ -500,7 +516,10 @@ def run_workload(args, wl, K, W, with_cpu, replays=5, ab_lib=None):
     else:
         sel = T == 1 and shared_runs_with_router(cfg, dtype, T)
         roofline = {
-            "kernel": ("moe::k_gemv_sel routed gate/up + SwiGLU (the selection in the same launch)"
+            "kernel": ("moe::k_gemv_sel routed gate/up + SwiGLU (the selection and the shared"
+                       " expert's down projection in the same launch)"
+                       if sel and shared_down_in_gate_up(cfg, dtype, T) else
+                       "moe::k_gemv_sel routed gate/up + SwiGLU (the selection in the same launch)"
                        if sel else
                        "moe::k_gemv gate/up + SwiGLU (routed experts)"
                        if shared_runs_with_router(cfg, dtype, T) else

@@ -24,8 +24,13 @@ def test_decode_gate_up_bytes_closed_form():
     h_out = K * I * 4               # one f32 h row per slot
     want = K * (codes + scales) + x_in + h_out
     assert want == 100_884_480
+    # the launch also runs the shared expert's down projection: its bf16
+    # [H][I] weights, its f32 h row in, its f32 output row out
+    s_down = H * I * 2 + I * 4 + H * 4
     assert bench.shared_runs_with_router(cfg, gen.I4, 1)
-    assert bench.gate_up_bytes(cfg, gen.I4, K, 1) == want
+    assert bench.shared_down_in_gate_up(cfg, gen.I4, 1)
+    assert bench.gate_up_bytes(cfg, gen.I4, K, 1) == want + s_down
+    assert want + s_down == 126_083_072
 
 
 def test_decode_gate_up_bytes_shared_in_launch():
