@@ -69,6 +69,7 @@ class Hip:
         L.hipStreamEndCapture.argtypes = [vp, P(vp)]
         L.hipGraphInstantiate.argtypes = [P(vp), vp, vp, vp, ctypes.c_size_t]
         L.hipGraphLaunch.argtypes = [vp, vp]
+        L.hipGraphUpload.argtypes = [vp, vp]
         self.L = L
 
     def _ok(self, rc, what):
@@ -108,6 +109,11 @@ class Hip:
 
     def launch(self, exe: int, stream: int):
         self._ok(self.L.hipGraphLaunch(exe, stream), "hipGraphLaunch")
+
+    def upload(self, exe: int, stream: int):
+        """Move an instantiated graph's work to the device ahead of its first
+        launch (runs none of its nodes)."""
+        self._ok(self.L.hipGraphUpload(exe, stream), "hipGraphUpload")
 
 
 # ------------------------------------------------ counter-measured traffic
@@ -448,6 +454,9 @@ def run_workload(args, wl, K, W, with_cpu, replays=5, ab_lib=None):
         ge = hip.capture(sh, lambda: [step(i, True) for i in range(K)])
         gb = hip.capture(sh, lambda: [step(i, False, whole=True) for i in range(K)])
         hip.launch(gw, sh)
+        # the timed graph is uploaded before the timed region (its first
+        # launch would otherwise carry the upload of its 3K nodes)
+        hip.upload(gt, sh)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         hip.launch(gt, sh)
