@@ -49,9 +49,11 @@ static_assert(sizeof(SelScratch) <= sizeof(RingLds::ring), "selection scratch fi
 // rows o0 + w - 1, o0 + w - 1 + (kWaves - 1), ...  A lane holds granules j,
 // j + 64, j + 128, j + 192 of a kSdnIs-wide row (8 bf16 weights each) and the
 // matching 32 values of h; the rows of a pass are requested together, then
-// each is dotted, summed over the wave and written.
-template <int ABF16>
-__device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave) {
+// each is dotted, summed over the wave and written.  load_x issues the wave's
+// other loads behind the first pass's rows (loads complete in issue order, so
+// the rows are not held up behind them).
+template <int ABF16, class XL>
+__device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave, XL&& load_x) {
   constexpr int EPG = Fmt<MOE_BF16>::EPG;
   constexpr int GPL = kSdnIs / kWave / EPG;
   constexpr int KSL = GPL * EPG;
@@ -62,11 +64,14 @@ __device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave) {
   const int lane = threadIdx.x & 63;
   const int o0 = (int)blockIdx.x * p.sdn_rpb;
   const int o1 = min(p.H, o0 + p.sdn_rpb);
-  if (o0 + wave - 1 >= o1) return;
+  if (o0 + wave - 1 >= o1) {
+    load_x();
+    return;
+  }
   const uint8_t* wl = p.sdn + lane * 16;
   u32x4 hr[slice_pieces<EPG, GPL, ABF16>()];
   slice_raw_load<EPG, GPL, ABF16>(p.sdn_h, 0, hr);
-  for (int r0 = o0 + wave - 1; r0 < o1; r0 += NW * RW) {
+  auto pass = [&](int r0, auto first) {
     u32x4 v[RW][GPL];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -77,6 +82,7 @@ __device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave) {
                                reinterpret_cast<const u32x4*>(wl + (int64_t)o * RB + g * 1024))
                          : u32x4{0u, 0u, 0u, 0u};
     }
+    if constexpr (decltype(first)::value) load_x();
     float x[1][KSL], gs[GPL];
     slice_raw_finish<EPG, GPL, ABF16>(hr, x[0], gs);
 #pragma unroll
@@ -91,7 +97,9 @@ __device__ __forceinline__ void shared_down_rows(const PreArgs& p, int wave) {
       const float sum = group_sum(acc[0], 64);
       if (o < o1 && lane == 0) p.sdn_out[o] = sum;
     }
-  }
+  };
+  pass(o0 + wave - 1, std::true_type{});
+  for (int r0 = o0 + wave - 1 + NW * RW; r0 < o1; r0 += NW * RW) pass(r0, std::false_type{});
 }
 
 template <int WR, int KR, int EPL, int ABF16, bool SDN>
@@ -103,9 +111,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Wave 0 selects: its candidate loads go out first.  The token's
   // activation slice (sliced row 0: every routed row of a one-token step is
-  // token 0) does not depend on the routing: its loads follow, so that they
-  // have landed when the block's ring starts, and the ring's whole first fill
-  // is issued at once.
+  // token 0) does not depend on the routing: its loads follow (in the other
+  // waves, behind their first shared down rows), so that they have landed
+  // when the block's ring starts, and the ring's whole first fill is issued
+  // at once.
   double ra[EPL], rb[EPL];
   if (wave == 0) {
     if (p.sp.softmax) select_load<EPL, true>(p.sp, p.zin, p.bias, nullptr, ra, rb);
@@ -113,15 +122,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
   constexpr int GPL = KR / Fmt<WR>::EPG;
   float xpre[KR], gpre[GPL];
-  {
+  auto load_x = [&]() {
     const int64_t xo0 = 0;
     float (&xv)[1][KR] = *reinterpret_cast<float (*)[1][KR]>(&xpre[0]);
     slices_sliced_load<Fmt<WR>::EPG, KR, 1, ABF16>(a.x, &xo0, 1, xv);
-  }
+  };
   if constexpr (SDN) {
+    if (wave == 0) load_x();
     // wave 0's candidate loads are out before the other waves' shared rows
     asm volatile("s_barrier" ::: "memory");
-    if (wave > 0) shared_down_rows<ABF16>(p, wave);
+    if (wave > 0) shared_down_rows<ABF16>(p, wave, load_x);
+  } else {
+    load_x();
   }
   SlotTables tb;
   tb.slot_tab = S.slot_tab;
