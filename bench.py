@@ -124,7 +124,7 @@ class Hip:
 # changes the counters no longer describe it and the traffic is reported null.
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "k_gemv_gate_up__glm_layer_decode_1tok.md")
 TRAFFIC_SOURCES = ["gemv_impl.h", "route_device.h", "unpack.h", "k_gemv.hip", "k_gemv_sel.hip",
-                   "moe_internal.h", "moe_capi.cpp"]
+                   "down_fused.h", "moe_internal.h", "moe_capi.cpp"]
 
 
 def kernel_sources_digest() -> str:
