@@ -288,6 +288,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
       }
     }
   }
+  // h was requested before the records and has landed with them; said
+  // here for every path, so that the compiler's own wait before h's first
+  // use does not become a wait for the ring's whole first fill
+  wait_vmcnt<0>();
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     ue[u] = __builtin_amdgcn_readfirstlane(ue[u]);
@@ -296,10 +300,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 8))
   }
   nu = __builtin_amdgcn_readfirstlane(nu);
   // a record whose row is not at its slot's position (not a one-token
-  // grouping): that row again, from where the record puts it
+  // grouping): that row again, from where the record puts it, waited for
+  // here (no h load is pending past this point)
 #pragma unroll
   for (int u = 0; u < 2; ++u)
-    if (u < nu && uh[u] != wave + u * kWaves) load_h(u, uh[u]);
+    if (u < nu && uh[u] != wave + u * kWaves) {
+      load_h(u, uh[u]);
+      wait_vmcnt<0>();
+    }
   // row scales of the wave's units, by direct loads into LDS (lane l fills
   // entry l; lanes past the block's rows reload its last row); the ring's
   // first wait covers them, as they are issued before its loads
